@@ -1,0 +1,162 @@
+/*
+ * ra.h -- C ABI of libra.so: one ring rank's share of causal blockwise
+ * attention on an AMD Instinct MI355X (gfx950).
+ *
+ * Ring Attention / context parallelism splits a sequence of S tokens over N
+ * devices. Each device keeps its query chunk, attends with the K/V chunk it
+ * holds, then receives the chunk of device i-1 and passes its own to i+1,
+ * until every query has met every key (discosf.com article, §3.1 环形通信拓扑;
+ * digipub.cc "大模型如何訓練百萬 Token 上下文", section "Zig Zag Ring
+ * Attention"). This library is the work one device does per received chunk:
+ * fold the chunk into running max / sum / output accumulators by an online
+ * softmax (intelliparadigm.com long-context survey, §3.1.2
+ * FlashAttention的核心算法), with the causal mask and an optional ALiBi bias
+ * (same survey, §2.1.2) both driven by GLOBAL token positions, so the
+ * contiguous split (discosf.com, §2.1 序列切分策略对比) and the zig-zag
+ * assignment (token i -> rank i mod N, digipub.cc section above) give the same
+ * attention.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *    The library allocates no device memory and keeps no mutable global state
+ *    besides the thread-local error text; calls from several host threads are
+ *    safe.
+ *  - Tensors are dense and row-major in the order written: [B, H, L, D] has D
+ *    fastest. Positions are int32 and shared by all batches and heads.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    runs asynchronously: RA_OK means "validated and enqueued".
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is launched and ra_last_error() describes the problem.
+ *  - A dimension of zero (empty batch, heads or lengths) is valid and
+ *    enqueues nothing.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ra_status {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, negative size, bad enum, inconsistent shape */
+  RA_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (e.g. head_dim) */
+  RA_ERR_HIP = 3               /* the HIP runtime reported an error on launch */
+} ra_status;
+
+typedef enum ra_dtype { RA_BF16 = 0, RA_FP32 = 1 } ra_dtype;
+
+typedef enum ra_layout {
+  RA_CONTIGUOUS = 0, /* rank r holds tokens [r*C, (r+1)*C) */
+  RA_ZIGZAG = 1      /* rank r holds tokens r, r+N, r+2N, ... (token i -> rank i mod N) */
+} ra_layout;
+
+/* Shapes of one attention step. len_q is the local query chunk length, len_kv
+ * the length of the K/V chunk being folded in. heads_q must be a multiple of
+ * heads_kv; query head h reads key/value head h / (heads_q / heads_kv).
+ * head_dim: 64 or 128 for RA_BF16; 1..128 for RA_FP32. */
+typedef struct ra_dims {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;
+  int32_t len_q;
+  int32_t len_kv;
+  int32_t dtype; /* ra_dtype of q, k, v, o and d_o */
+} ra_dims;
+
+/* Global positions of the tokens rank `rank` holds, in local row order
+ * (increasing), for a sequence of seq_len tokens over n_ranks ranks:
+ * contiguous r*C + t, zig-zag t*N + r, with C = seq_len / n_ranks
+ * (discosf.com §2.1; digipub.cc "Zig Zag Ring Attention").
+ * rank = -1 writes all ranks: pos_out is int32 [n_ranks, C]; otherwise [C].
+ * Errors: seq_len not a positive multiple of n_ranks, seq_len/n_ranks or
+ * seq_len above INT32_MAX, bad layout or rank, pos_out NULL. */
+ra_status ra_positions(int64_t seq_len, int32_t n_ranks, int32_t rank, int32_t layout,
+                       int32_t* pos_out, void* stream);
+
+/* Layout permutation between global sequence order and rank-major chunks.
+ * `outer` independent slabs (B*H for a [B,H,S,D] tensor) of seq_len rows of
+ * row_elems elements of `dtype` each.
+ *   inverse = 0: src is global [outer, S, row]; dst is [n_ranks, outer, C, row]
+ *                when rank = -1, or [outer, C, row] holding only that rank;
+ *                dst[r][o][t] = src[o][pos_r(t)].
+ *   inverse = 1: the reverse gather; src is rank-major ([n_ranks, outer, C,
+ *                row], or [outer, C, row] for one rank) and dst is global
+ *                [outer, S, row]; with rank >= 0 only that rank's rows of dst
+ *                are written.
+ * pos (may be NULL) also receives the positions as ra_positions writes them.
+ * src and dst must not overlap. Pure data movement: bit-exact. */
+ra_status ra_layout_permute(const void* src, void* dst, int32_t* pos, int64_t outer,
+                            int64_t seq_len, int32_t row_elems, int32_t dtype, int32_t n_ranks,
+                            int32_t layout, int32_t rank, int32_t inverse, void* stream);
+
+/* Start state of the running accumulators: o_acc = 0 [B,Hq,Lq,D], m = -inf and
+ * l = 0 [B,Hq,Lq] (the initial max and sum of the online softmax,
+ * intelliparadigm.com §3.1.2). All fp32. Only batch, heads_q, head_dim and
+ * len_q of d are used. */
+ra_status ra_state_init(const ra_dims* d, float* o_acc, float* m, float* l, void* stream);
+
+/* One ring step: fold the K/V chunk (k_blk, v_blk: [B, Hkv, Lkv, D]) into the
+ * running state of the local queries q [B, Hq, Lq, D].
+ *
+ * Scores are s = scale * <q_i, k_j> - slope_h * |q_pos[i] - k_pos[j]| (the
+ * ALiBi term only when alibi_slopes != NULL, alibi_slopes being fp32 [Hq]);
+ * with causal != 0 a key is visible only if k_pos[j] <= q_pos[i].
+ * The state, all fp32 and updated in place, is defined over the keys J folded
+ * in so far: m = max_J s, l = sum_J exp(s - m), o_acc = sum_J exp(s - m) v_j
+ * (natural exponent). Rows with no visible key keep m = -inf, l = 0,
+ * o_acc = 0. Chunks may be folded in any order; the result differs only by
+ * rounding.
+ * q_pos [Lq] and k_pos [Lkv] must be strictly increasing (both layouts give
+ * that); tiles that are masked out entirely are skipped using this.
+ * Positions must be non-negative. For bf16, q, k_blk, v_blk and o_acc must be
+ * 16-byte aligned (RA_ERR_INVALID_ARGUMENT otherwise).
+ * Computation: bf16 inputs use bf16 MFMA with fp32 accumulation (P is rounded
+ * to bf16 before the P.V product); fp32 inputs are computed in fp32. */
+ra_status ra_step_fwd(const ra_dims* d, const void* q, const void* k_blk, const void* v_blk,
+                      const int32_t* q_pos, const int32_t* k_pos, int32_t causal, float scale,
+                      const float* alibi_slopes, float* o_acc, float* m, float* l, void* stream);
+
+/* Normalise after the last step: o = o_acc / l in d->dtype (bf16 round to
+ * nearest even) and lse = m + ln(l) in fp32 (intelliparadigm.com §3.1.2, the
+ * final division by l). Rows with l = 0 give o = 0 and lse = -inf.
+ * o: [B,Hq,Lq,D]; lse: [B,Hq,Lq]; either may be NULL to skip it. */
+ra_status ra_finalize(const ra_dims* d, const float* o_acc, const float* m, const float* l,
+                      void* o, float* lse, void* stream);
+
+/* Backward pre-pass, once per ring pass: delta[i] = sum_d d_o[i,d] * o[i,d]
+ * (fp32 [B,Hq,Lq]), the row term of the softmax gradient. o and d_o are
+ * [B,Hq,Lq,D] in d->dtype. */
+ra_status ra_bwd_delta(const ra_dims* d, const void* o, const void* d_o, float* delta,
+                       void* stream);
+
+/* One backward ring step for the K/V chunk (k_blk, v_blk). The pages only say
+ * that the backward recomputes attention from saved statistics instead of
+ * storing it (intelliparadigm.com §3.1.2); the gradients are the textbook
+ * ones, with P recomputed from the final lse of ra_finalize:
+ *   P = exp(s - lse), dS = P * (d_o . v^T - delta),
+ *   dq_acc += scale * dS k,  dk_blk += scale * dS^T q,  dv_blk += P^T d_o.
+ * Same masking, positions and ALiBi term as ra_step_fwd. dq_acc
+ * [B,Hq,Lq,D], dk_blk and dv_blk [B,Hkv,Lkv,D] are fp32 and ACCUMULATE
+ * (caller zeroes them once); query heads sharing a K/V head add into it.
+ * Supported for RA_BF16 with head_dim 128; deterministic (no atomics). */
+ra_status ra_step_bwd(const ra_dims* d, const void* q, const void* k_blk, const void* v_blk,
+                      const int32_t* q_pos, const int32_t* k_pos, int32_t causal, float scale,
+                      const float* alibi_slopes, const void* d_o, const float* lse,
+                      const float* delta, float* dq_acc, float* dk_blk, float* dv_blk,
+                      void* stream);
+
+/* Text for the last non-OK status returned on this host thread ("" if none). */
+const char* ra_last_error(void);
+
+/* Version of this library's ABI (increments on incompatible change). */
+int32_t ra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

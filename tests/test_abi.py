@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/ra.h declares, and rejects invalid arguments before
+launching anything. Also the binding's host logic (ring order, slopes)."""
+
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_attention_ra_amd import _lib, configs, ring
+
+L = _lib.lib()
+
+
+def _dims(b=1, hq=2, hkv=2, d=128, lq=128, lkv=128, dt=_lib.RA_BF16):
+    return _lib.RaDims(b, hq, hkv, d, lq, lkv, dt)
+
+
+def _fwd(dims, ptr=1, scale=0.1, slopes=None):
+    return L.ra_step_fwd(None if dims is None else ctypes.byref(dims), ptr, ptr, ptr, ptr, ptr, 1, scale,
+                         slopes, ptr, ptr, ptr, None)
+
+
+def test_exports_every_declared_symbol():
+    names = _lib.header_symbols()
+    assert set(names) >= {"ra_layout_permute", "ra_step_fwd", "ra_finalize", "ra_step_bwd", "ra_positions",
+                          "ra_state_init", "ra_bwd_delta", "ra_last_error", "ra_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.ra_abi_version() == 1
+
+
+@pytest.mark.parametrize("dims,status,needle", [
+    (None, 1, "dims is NULL"),
+    (_dims(hq=3, hkv=2), 1, "multiple of heads_kv"),
+    (_dims(hkv=0), 1, "multiple of heads_kv"),
+    (_dims(d=96), 2, "head_dim"),
+    (_dims(d=129, dt=_lib.RA_FP32), 2, "head_dim"),
+    (_dims(d=0), 1, "head_dim"),
+    (_dims(lq=-1), 1, "negative"),
+    (_dims(dt=7), 1, "dtype"),
+])
+def test_step_fwd_validation(dims, status, needle):
+    assert _fwd(dims) == status
+    assert needle in _lib.ra_last_error()
+
+
+def test_step_fwd_null_pointer_and_scale():
+    assert _fwd(_dims(), ptr=None) == 1 and "NULL" in _lib.ra_last_error()
+    assert _fwd(_dims(), scale=float("nan")) == 1 and "scale" in _lib.ra_last_error()
+    assert _fwd(_dims(), scale=float("inf")) == 1
+
+
+def test_empty_work_is_ok_without_launch():
+    assert _fwd(_dims(lkv=0), ptr=None) == 0
+    assert _fwd(_dims(lq=0), ptr=None) == 0
+    assert _fwd(_dims(b=0), ptr=None) == 0
+    assert L.ra_finalize(ctypes.byref(_dims()), None, None, None, None, None, None) == 0
+    assert L.ra_layout_permute(None, None, None, 0, 16, 8, 0, 4, 0, -1, 0, None) == 0
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((16, 0, -1, 0), "n_ranks"),
+    ((18, 4, -1, 0), "multiple"),
+    ((16, 4, 4, 0), "rank"),
+    ((16, 4, -2, 0), "rank"),
+    ((16, 4, 0, 5), "layout"),
+    ((2 ** 31, 4, 0, 0), "int32"),
+])
+def test_positions_validation(args, needle):
+    s, n, r, lay = args
+    assert L.ra_positions(s, n, r, lay, 1, None) == 1
+    assert needle in _lib.ra_last_error()
+    assert L.ra_positions(16, 4, 0, 0, None, None) == 1
+
+
+def test_permute_validation():
+    buf = ctypes.create_string_buffer(4096)
+    base = ctypes.addressof(buf)
+    # overlapping src/dst
+    assert L.ra_layout_permute(base, base + 16, None, 1, 16, 8, 0, 4, 0, -1, 0, None) == 1
+    assert "overlap" in _lib.ra_last_error()
+    assert L.ra_layout_permute(base, base + 2048, None, 1, 16, 8, 0, 4, 0, -1, 2, None) == 1
+    assert L.ra_layout_permute(base, base + 2048, None, 1, 16, 0, 0, 4, 0, -1, 0, None) == 1
+    assert L.ra_layout_permute(base, base + 2048, None, 1, 16, 8, 3, 4, 0, -1, 0, None) == 1
+    assert L.ra_layout_permute(None, base, None, 1, 16, 8, 0, 4, 0, -1, 0, None) == 1
+
+
+def test_bwd_validation():
+    d = _dims(dt=_lib.RA_FP32, d=64)
+    args = [ctypes.byref(d)] + [1] * 5 + [1, 0.1, None] + [1] * 6 + [None]
+    assert L.ra_step_bwd(*args) == 2 and "bf16" in _lib.ra_last_error()
+    d = _dims()
+    args = [ctypes.byref(d)] + [1] * 5 + [1, 0.1, None] + [1] * 5 + [None, None]
+    assert L.ra_step_bwd(*args) == 1
+
+
+def test_binding_checks_tensors():
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        _lib._ptr(t, "t")  # host tensor
+    with pytest.raises(ValueError):
+        _lib.dtype_code(torch.float16)
+
+
+def test_ring_schedule_and_slopes_agree_with_oracle():
+    for n in (1, 4, 8, 64):
+        for r in range(n):
+            assert ring.ring_schedule(n, r) == oracle.ring_schedule(n, r)
+    for h in (1, 8, 16, 64):
+        got = ring.alibi_slopes(h, device="cpu").numpy()
+        np.testing.assert_array_equal(got, oracle.alibi_slopes(h).astype(np.float32))
+
+
+def test_workloads_match_their_names():
+    assert len(configs.WORKLOADS) == 5
+    for w in configs.WORKLOADS:
+        assert w.seq_len % w.n_ranks == 0 and 0 <= w.rank < w.n_ranks
+        assert w.heads_q % w.heads_kv == 0
+    assert configs.HEADLINE.seq_len == 131072 and configs.HEADLINE.layout == "zigzag"
+    assert math.isclose(configs.get(4).std ** 2, 0.5)
