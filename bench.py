@@ -1,0 +1,262 @@
+"""Benchmark: one ring rank's share of causal attention on one MI355X.
+
+A step is one pass of the whole path for the rank under study: the layout
+permutation of its query chunk and of every K/V chunk out of global order
+(ra_layout_permute), the accumulator start state, one ra_step_fwd per chunk
+in ring order, ra_finalize, and -- for the workload that has one -- the
+backward ring (ra_bwd_delta + one ra_step_bwd per chunk). Inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts.
+
+Prints one JSON line. `value` is causal-effective TFLOP/s of the whole step
+(forward 4*D FLOP per visible (query, key) pair per query head, backward
+10*D). `roofline` is the dominant kernel (the bf16 step kernel) timed live
+with HIP events on the stream it runs on. `cpu_baseline` is the fp64 oracle
+timed on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import seeded_inputs as si  # noqa: E402
+from ring_attention_ra_amd import _lib, configs, ring  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+
+def visible_pairs_per_chunk(w, pos_cpu):
+    """Visible (query, key) pairs per head for each ring step of the rank."""
+    qp = pos_cpu[w.rank]
+    out = []
+    for s in ring.ring_schedule(w.n_ranks, w.rank):
+        kp = pos_cpu[s]
+        if w.causal:
+            out.append(int(torch.searchsorted(kp, qp, right=True).sum()))
+        else:
+            out.append(int(qp.numel() * kp.numel()))
+    return out
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=str(configs.HEADLINE.index),
+                    help="workload index (1-5) or name; default: the 128K zig-zag share")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the CPU-baseline sample")
+    ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-baseline sample")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per step-kernel launch (from rocprofv3 counters)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, rows_n, heads_n):
+    """Time the fp64 oracle on a bounded sample: `heads_n` heads x `rows_n`
+    query rows spread evenly over the rank's chunk, all their visible keys."""
+    import numpy as np
+
+    import oracle
+
+    g = w.heads_q // w.heads_kv
+    heads = sorted({int(x) for x in np.linspace(0, w.heads_q - 1, heads_n).round()})
+    rows = np.unique(np.linspace(0, w.chunk - 1, rows_n).round().astype(np.int64))
+
+    def host(t, hs):
+        out = np.zeros(tuple(t.shape), dtype=np.float32)
+        for h in sorted(set(hs)):
+            out[:, h] = t[:, h].float().cpu().numpy()
+        return out
+
+    qh, kh, vh = host(q, heads), host(k, [h // g for h in heads]), host(v, [h // g for h in heads])
+    slopes = oracle.alibi_slopes(w.heads_q) if w.alibi else None
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.attention_rank_share(qh, kh, vh, w.n_ranks, w.rank, w.layout, w.causal, w.scale, slopes,
+                                rows=rows, heads=heads, threads=threads)
+    dt = time.perf_counter() - t0
+    pos = oracle.rank_positions(w.seq_len, w.n_ranks, w.rank, w.layout)[rows]
+    pairs = int((pos + 1).sum()) if w.causal else rows.size * w.seq_len
+    flops = 4.0 * w.head_dim * pairs * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle forward, {len(heads)} heads x {rows.size} query rows spread over the "
+                      f"rank's {w.chunk}-row chunk ({pairs * len(heads)} visible pairs, {dt:.1f} s)",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} is not supported "
+              "(the ring is simulated on a single device)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    _lib.lib()
+    w = configs.get(int(args.workload)) if args.workload.isdigit() else configs.get(args.workload)
+    dev = torch.device("cuda:0")
+    dt = si.torch_dtype(w.dtype)
+    b, hq, hkv, d, s, n, c = w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seq_len, w.n_ranks, w.chunk
+
+    # ---- inputs, resident in HBM ----
+    q_g = si.normal((b, hq, s, d), si.seed_for(w.index, si.Q_STREAM), w.std, w.dtype, dev)
+    k_g = si.normal((b, hkv, s, d), si.seed_for(w.index, si.K_STREAM), w.std, w.dtype, dev)
+    v_g = si.normal((b, hkv, s, d), si.seed_for(w.index, si.V_STREAM), w.std, w.dtype, dev)
+    d_o = si.normal((b, hq, c, d), si.seed_for(w.index, si.DO_STREAM), 1.0, w.dtype, dev) if w.backward else None
+    slopes = ring.alibi_slopes(hq, dev) if w.alibi else None
+
+    # ---- buffers, allocated once ----
+    q_loc = torch.empty((b, hq, c, d), dtype=dt, device=dev)
+    k_ch = torch.empty((n, b, hkv, c, d), dtype=dt, device=dev)
+    v_ch = torch.empty_like(k_ch)
+    pos = torch.empty((n, c), dtype=torch.int32, device=dev)
+    dims = _lib.make_dims(b, hq, hkv, d, c, c, dt)
+    o_acc = torch.empty((b, hq, c, d), dtype=torch.float32, device=dev)
+    m = torch.empty((b, hq, c), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    o = torch.empty((b, hq, c, d), dtype=dt, device=dev)
+    lse = torch.empty_like(m)
+    if w.backward:
+        delta = torch.empty_like(m)
+        dq = torch.empty((b, hq, c, d), dtype=torch.float32, device=dev)
+        dk = torch.empty((n, b, hkv, c, d), dtype=torch.float32, device=dev)
+        dv = torch.empty_like(dk)
+    sched = ring.ring_schedule(n, w.rank)
+    stream = torch.cuda.current_stream()
+
+    fwd_events, bwd_events, perm_events = [], [], []
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(timed):
+        if timed:
+            perm_events.append(ev())
+        _lib.ra_layout_permute(q_g, q_loc, None, b * hq, s, d, n, w.layout, rank=w.rank)
+        _lib.ra_layout_permute(k_g, k_ch, pos, b * hkv, s, d, n, w.layout, rank=-1)
+        _lib.ra_layout_permute(v_g, v_ch, None, b * hkv, s, d, n, w.layout, rank=-1)
+        if timed:
+            perm_events.append(ev())
+        _lib.ra_state_init(dims, o_acc, m, l)
+        for src in sched:
+            if timed:
+                fwd_events.append(ev())
+            _lib.ra_step_fwd(dims, q_loc, k_ch[src], v_ch[src], pos[w.rank], pos[src], w.causal, w.scale,
+                             slopes, o_acc, m, l)
+            if timed:
+                fwd_events.append(ev())
+        _lib.ra_finalize(dims, o_acc, m, l, o, lse)
+        if w.backward:
+            _lib.ra_bwd_delta(dims, o, d_o, delta)
+            dq.zero_()
+            dk.zero_()
+            dv.zero_()
+            for src in sched:
+                if timed:
+                    bwd_events.append(ev())
+                _lib.ra_step_bwd(dims, q_loc, k_ch[src], v_ch[src], pos[w.rank], pos[src], w.causal, w.scale,
+                                 slopes, d_o, lse, delta, dq, dk[src], dv[src])
+                if timed:
+                    bwd_events.append(ev())
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    pairs = visible_pairs_per_chunk(w, pos.cpu())
+    fwd_flops = 4.0 * d * hq * b * sum(pairs)
+    bwd_flops = 10.0 * d * hq * b * sum(pairs) if w.backward else 0.0
+    step_flops = fwd_flops + bwd_flops
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    def pair_ms(evs):
+        return [evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2)]
+
+    fwd_ms = pair_ms(fwd_events)
+    fwd_launch_ms = sum(fwd_ms) / len(fwd_ms)
+    fwd_total_ms = sum(fwd_ms) / args.steps
+    fwd_tflops = fwd_flops / (fwd_total_ms * 1e-3) / 1e12
+    perm_ms = sum(pair_ms(perm_events)) / args.steps
+    perm_bytes = 2.0 * (q_loc.numel() + k_ch.numel() + v_ch.numel()) * q_loc.element_size() + pos.numel() * 4
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+
+    extra = {
+        "step_kernel_tflops": round(fwd_tflops, 2),
+        "step_kernel_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "step_kernel_ms_per_step": round(fwd_total_ms, 4),
+        "permute_ms_per_step": round(perm_ms, 4),
+        "permute_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
+        "visible_pairs_per_head": sum(pairs),
+        "fwd_flop_per_step": fwd_flops,
+    }
+    if w.backward:
+        bwd_ms = pair_ms(bwd_events)
+        bwd_total_ms = sum(bwd_ms) / args.steps
+        extra["bwd_kernel_ms_per_step"] = round(bwd_total_ms, 4)
+        extra["bwd_kernel_tflops"] = round(bwd_flops / (bwd_total_ms * 1e-3) / 1e12, 2)
+        extra["bwd_flop_per_step"] = bwd_flops
+
+    result = {
+        "metric": "causal attention TFLOP/s per ring-rank share + % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0, std^2) inputs, see seeded_inputs.py)",
+        "config": w.describe(),
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round((fwd_flops / n) / (fwd_launch_ms * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": None,
+            "traffic": traffic,
+            "kernel": "fwd_bf16_kernel (ra_step_fwd)",
+            "launch_ms": round(fwd_launch_ms, 4),
+            "flop_per_launch": fwd_flops / n,
+        },
+        "breakdown": extra,
+    }
+    result["roofline"]["frac"] = round(result["roofline"]["achieved"] / PEAK_BF16_TFLOPS, 4)
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, q_g, k_g, v_g, args.cpu_rows, args.cpu_heads)
+        cb["value"] = round(cb["value"], 5)
+        cb.pop("seconds")
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
