@@ -15,7 +15,8 @@ import re
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libra.so")
+# RA_LIB may name another build of the same library (same ABI).
+LIB_PATH = os.environ.get("RA_LIB") or os.path.join(PKG, "libra.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "ra.h")
 
 RA_OK, RA_ERR_INVALID_ARGUMENT, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
