@@ -320,8 +320,13 @@ def attention_rank_share_bwd(q_g, k_g, v_g, do_local, n_ranks, rank, layout, cau
         kh_all = np.asarray(k_g[bi, hk], dtype=np.float64)
         vh_all = np.asarray(v_g[bi, hk], dtype=np.float64)
         # Rows whose gradients we need: the requested dQ rows, and every local
-        # row when key gradients are requested (dK_j sums over all rows p).
-        need_rows = np.arange(c) if want_keys else rows
+        # row that can see a requested key (dK_j sums over the rows p that see
+        # key j; under the causal mask a row p < min(keys) adds exact zeros).
+        if want_keys:
+            sees = pos >= keys.min() if causal else np.ones(c, dtype=bool)
+            need_rows = np.union1d(np.nonzero(sees)[0], rows)
+        else:
+            need_rows = rows
         dk_part = np.zeros((keys.size, d))
         dv_part = np.zeros((keys.size, d))
         dq_rows = {}

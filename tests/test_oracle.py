@@ -491,6 +491,11 @@ def test_bwd_subsets_match_full():
     np.testing.assert_allclose(sub[0], full[0][:, 2:4][:, :, rows], rtol=0, atol=1e-14)
     np.testing.assert_allclose(sub[1], full[1][:, 1:2][:, :, keys], rtol=0, atol=1e-14)
     np.testing.assert_allclose(sub[2], full[2][:, 1:2][:, :, keys], rtol=0, atol=1e-14)
+    # late keys only: rows that cannot see them are skipped, the result is unchanged
+    late = np.array([27, 30, 31])
+    sub = oracle.attention_rank_share_bwd(qg, kg, vg, do, n, 3, oracle.ZIGZAG, True, 0.5, rows=rows, keys=late)
+    np.testing.assert_allclose(sub[1], full[1][:, :, late], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(sub[2], full[2][:, :, late], rtol=0, atol=1e-14)
 
 
 # ---------------------------------------------------------------------------

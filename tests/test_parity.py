@@ -281,3 +281,91 @@ def test_fp32_finalize_of_unvisited_rows():
     o, lse = ring.finalize(st, torch.float32)
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+# ---------------------------------------------------------------------------
+# backward parity (bf16, D = 128): max |g - g_ref| <= 1e-2 * max |g_ref|
+# ---------------------------------------------------------------------------
+
+BWD_REL = 1e-2
+
+
+def _bwd_gpu(case, r, q, k, v, do):
+    q_loc, k_ch, v_ch, pos = ring.shard(q, k, v, case.n_ranks, case.layout, r)
+    sl = _slopes_dev(case)
+    o, lse = ring.forward(q_loc, k_ch, v_ch, pos, r, case.causal, case.sc(), sl)
+    dq, dk, dv = ring.backward(q_loc, k_ch, v_ch, pos, r, case.causal, case.sc(), sl, o, lse, do)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _rel_err(got, ref):
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    return max_abs(got, ref) / max(scale, 1e-30)
+
+
+@pytest.mark.parametrize("layout,causal,alibi,hq,hkv,n,c", [
+    ("zigzag", True, False, 2, 2, 4, 256),
+    ("contiguous", True, False, 4, 2, 4, 192),     # GQA, ragged tiles
+    ("zigzag", True, True, 2, 1, 2, 320),          # ALiBi + GQA, ragged
+    ("contiguous", False, False, 2, 2, 2, 200),    # no mask, ragged
+    ("contiguous", True, True, 2, 2, 3, 128),
+])
+def test_bwd_variants(layout, causal, alibi, hq, hkv, n, c):
+    case = Case("bf16", 1, hq, hkv, 128, n * c, n, layout, causal, alibi, seed=61)
+    log(f"case {case.tag()}")
+    q, k, v, do = draw(case, with_do=True)
+    qh, kh, vh = host64(q), host64(k), host64(v)
+    for r in sorted({0, n - 1}):
+        dq, dk, dv = _bwd_gpu(case, r, q, k, v, do)
+        dq_r, dk_r, dv_r = oracle.attention_rank_share_bwd(qh, kh, vh, host64(do), n, r, layout, causal, case.sc(),
+                                                           oracle_slopes(case))
+        e_q = _rel_err(host64(dq), dq_r)
+        e_k = _rel_err(host64(dk), oracle.permute_to_ranks(dk_r, n, layout))
+        e_v = _rel_err(host64(dv), oracle.permute_to_ranks(dv_r, n, layout))
+        log(f"  rank {r}: rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g}")
+        assert e_q <= BWD_REL and e_k <= BWD_REL and e_v <= BWD_REL
+
+
+def test_bwd_deterministic():
+    case = Case("bf16", 1, 2, 2, 128, 4 * 256, 4, "zigzag", True, False, seed=63)
+    q, k, v, do = draw(case, with_do=True)
+    a = [t.cpu().numpy().tobytes() for t in _bwd_gpu(case, 3, q, k, v, do)]
+    b = [t.cpu().numpy().tobytes() for t in _bwd_gpu(case, 3, q, k, v, do)]
+    assert a == b
+
+
+def test_workload_1m_zigzag_backward_sampled():
+    """Full-size forward + backward of the 1M-token zig-zag share; the oracle
+    recomputes dQ on sampled rows and dK, dV on sampled late keys (few rows see
+    them under the causal mask) for two heads."""
+    w = configs.get(5)
+    case = Case(w.dtype, w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seq_len, w.n_ranks, w.layout,
+                w.causal, w.alibi, w.std, seed=w.index)
+    log(f"case {w.name} (backward, sampled)")
+    with Timer("draw + GPU forward/backward"):
+        q, k, v, do = draw(case, with_do=True)
+        dq, dk, dv = _bwd_gpu(case, w.rank, q, k, v, do)
+    heads = [0, w.heads_q - 1]
+    c, n, s = w.chunk, w.n_ranks, w.seq_len
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(c - 8, c), rng.integers(0, c, 16)]))
+    keys = np.unique(np.concatenate([np.arange(s - 24, s), rng.integers(s - 4096, s, 8)]))
+    with Timer("host copies"):
+        qh, kh, vh = host_heads(q, heads), host_heads(k, heads), host_heads(v, heads)
+        doh = do.float().cpu().numpy()
+    with Timer("oracle"):
+        dq_r, dk_r, dv_r = oracle.attention_rank_share_bwd(qh, kh, vh, doh, n, w.rank, w.layout, w.causal,
+                                                           w.scale, None, rows=rows, keys=keys, kv_heads=heads)
+    owner = oracle.owner_rank(keys, s, n, w.layout)
+    local = keys // n if w.layout == "zigzag" else keys % c
+    hsel = torch.tensor(heads, device=dk.device)
+    dk_g = np.stack([host64(dk[int(owner[i])].index_select(1, hsel)[:, :, int(local[i])])
+                     for i in range(keys.size)], axis=2)
+    dv_g = np.stack([host64(dv[int(owner[i])].index_select(1, hsel)[:, :, int(local[i])])
+                     for i in range(keys.size)], axis=2)
+    dq_g = host64(dq[:, heads][:, :, rows])
+    e_q, e_k, e_v = _rel_err(dq_g, dq_r), _rel_err(dk_g, dk_r), _rel_err(dv_g, dv_r)
+    log(f"  rows={rows.size} keys={keys.size}: rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g}")
+    assert e_q <= BWD_REL and e_k <= BWD_REL and e_v <= BWD_REL
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
