@@ -17,6 +17,7 @@ timed on a bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -58,8 +59,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the CPU-baseline sample")
     ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-baseline sample")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per step-kernel launch (from rocprofv3 counters)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fwd_bf16_128k_zigzag_traffic.json"),
+                    help="JSON with counter-measured HBM bytes per step-kernel launch; used only when it was "
+                         "taken on this workload and on the current kernel source")
     return ap.parse_args()
 
 
@@ -203,7 +205,12 @@ def main():
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
         with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+            rec = json.load(f)
+        src = os.path.join(ROOT, "ring_attention_ra_amd", "csrc", "fwd_bf16.hip")
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("kernel_source_sha256") == sha and rec.get("workload") == w.name:
+            traffic = rec.get("bytes_per_launch")
 
     extra = {
         "step_kernel_tflops": round(fwd_tflops, 2),
