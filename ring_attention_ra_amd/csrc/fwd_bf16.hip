@@ -9,12 +9,11 @@
 // exp(m_old - m_new) and every term taken against the same reference max.
 //
 // How it maps onto the MI355X:
-//  * One 256-thread work-group (4 waves) owns 128 query rows of one head;
+//  * One 512-thread work-group (8 waves) owns 256 query rows of one head;
 //    each wave owns 32 rows. K/V stream through a double-buffered LDS tile of
 //    64 keys, moved global -> LDS by the DMA path (global_load_lds_dwordx4, no
-//    register staging) while the previous tile is computed; one barrier per
-//    tile. Rows past the end of the chunk are clamped to the last key and
-//    masked.
+//    register staging). Rows past the end of the chunk are clamped to the
+//    last key and masked.
 //  * The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every
 //    lane holds the scores of ONE query (its column) against 16 keys of a
 //    32-key block. Row max needs one cross-half exchange (v_permlane32_swap);
@@ -27,6 +26,19 @@
 //    the row-major V tile with ds_read_b64_tr_b16, whose 16-lane transpose
 //    turns "lane j' addresses V[k0 + j'/4][d0 + 4*(j'%4)]" into "lane j holds
 //    V[k0 .. k0+3][d0 + j]". The output accumulator keeps one query per lane.
+//  * Ping-pong between two sets of four waves (one wave of each set per
+//    SIMD): over the tiles that every row of the work-group sees in full,
+//    both sets run "MFMA phase | barrier | softmax phase | barrier" with set 1
+//    one phase behind set 0, so on each SIMD one wave's matrix products
+//    overlap the other wave's exponentials. An MFMA phase is the P.V product
+//    of the previous tile and the QK product of the current one; its LDS
+//    fragment reads run four MFMAs ahead of use. Set 0 issues the copies of
+//    the next K and current V tile at the start of its MFMA phase and waits
+//    for them before the next barrier. Empty volatile asm statements pin each
+//    phase's results and scheduling barriers keep the compiler from moving
+//    work across the work-group barriers. The remaining tiles (diagonal,
+//    ragged, or ALiBi without the causal mask) follow one at a time with all
+//    waves in step and per-element masks where needed.
 //  * The output is rescaled lazily: exponents are taken against a reference
 //    max that is raised (and O, l rescaled) only when a score exceeds it by
 //    more than 2^8; P then stays below 2^8, well inside bf16 / fp32 range. The
@@ -35,18 +47,15 @@
 //    l = sum exp(s - m), o_acc = sum exp(s - m) v.
 //  * Scores are kept in base-2 units (scale * log2 e folded into one FMA) and
 //    exponentiated with v_exp_f32; state in memory is in natural units.
-//  * Tile classes, all chosen with wave-uniform scalar branches: key tiles
-//    past the last query of the work-group are never visited (positions
-//    increase); a wave skips tiles entirely in its causal future; tiles that
-//    every row of the wave sees in full take the fast path (raw row max, one
-//    FMA + one exp per score); only tiles across the diagonal or past the end
-//    of the chunk are masked per element. Under the causal mask the ALiBi term
-//    of a fully visible tile is linear in the key position, so it becomes one
-//    per-key term staged in LDS plus one per-row constant.
+//  * Key tiles past the last query of the work-group are never visited
+//    (positions increase); a wave skips tiles entirely in its causal future.
+//    Under the causal mask the ALiBi term of a fully visible tile is linear
+//    in the key position, so it becomes one per-key term staged in LDS plus
+//    one per-row constant.
 //  * Work-groups are ordered heaviest-first and, when the counts allow, each
 //    XCD is given whole heads so that its L2 serves one head's K/V stream.
 //  * LDS rows are XOR-swizzled in 16-byte units so that the fragment reads of
-//    a wave hit distinct banks.
+//    a wave spread over the banks.
 #include <type_traits>
 
 #include "ra_internal.h"
@@ -54,9 +63,10 @@
 namespace ra {
 namespace {
 
-constexpr int BM = 128;  // query rows per work-group
+constexpr int BM = 256;  // query rows per work-group (two sets of 4 waves x 32 rows)
 constexpr int BN = 64;   // keys per tile
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
 
 enum TileMode { kFast = 0, kAlibiLinear = 1, kExact = 2 };
@@ -100,14 +110,35 @@ __device__ __forceinline__ uint2 lds_tr4(const void* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Scheduling pattern of one MFMA phase: NPV P.V products (two transposing LDS
+// reads each) followed by NQK QK products (one LDS read each). The reads of
+// the first four products go first; after product i come the reads of
+// product i + 4.
+template <int NPV, int NQK, int I>
+__device__ __forceinline__ void interleave_step() {
+  if constexpr (I < NPV + NQK) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (I + 4 < NPV + NQK) {
+      __builtin_amdgcn_sched_group_barrier(0x100, (I + 4 < NPV ? 2 : 1), 0);  // LDS reads
+    }
+    interleave_step<NPV, NQK, I + 1>();
+  }
+}
+template <int NPV, int NQK>
+__device__ __forceinline__ void interleave_mfma_reads() {
+  constexpr int first = (NPV >= 4 ? 8 : 2 * NPV + (4 - NPV));
+  __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
+  interleave_step<NPV, NQK, 0>();
+}
+
 template <int D, bool ALIBI>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(StepArgs a, int n_qtiles,
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n_qtiles,
                                                                 int xcd_remap) {
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
   constexpr int KK = D / 16;            // k-steps of the QK product
   constexpr int DT = D / 32;            // 32-row d tiles of O^T
   constexpr int SLOTS = BN * CPR;       // 16-byte slots in a K (or V) tile
-  constexpr int DMA_PER_WAVE = SLOTS / (4 * 64);
+  constexpr int DMA_PER_WAVE = SLOTS / (kWaves * 64);
 
   __shared__ uint4 Ks[2][SLOTS];
   __shared__ uint4 Vs[2][SLOTS];
@@ -128,6 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(StepArgs a, int n
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int set = wave >> 2;  // two sets of 4 waves, half a tile apart
   const int q0 = qt * BM, q0w = q0 + wave * 32;
   const int row = q0w + l32;
   const bool row_ok = row < Lq;
@@ -144,9 +176,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(StepArgs a, int n
   const int* kpos = a.k_pos;
   const bool causal = a.causal != 0;
 
+  // Tiles the work-group visits: keys up to its last query (positions increase).
   const int qmax_wg = a.q_pos[min(q0 + BM - 1, Lq - 1)];
-  auto tile_live = [&](int kv0) { return kv0 < Lkv && (!causal || kpos[kv0] <= qmax_wg); };
-  if (!tile_live(0)) return;  // nothing visible: the state is unchanged
+  int T = (Lkv + BN - 1) / BN;
+  if (causal) {
+    int lo = 0, hi = T;  // first tile whose first key is past qmax_wg
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (kpos[mid * BN] <= qmax_wg) lo = mid + 1; else hi = mid;
+    }
+    T = lo;
+  }
+  if (T == 0) return;  // nothing visible: the state is unchanged
 
   const int qmin_w = wave_active ? a.q_pos[q0w] : INT32_MAX;
   const int qmax_w = wave_active ? a.q_pos[min(q0w + 31, Lq - 1)] : INT32_MIN;
@@ -155,20 +196,43 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(StepArgs a, int n
   const bool fast_ok = c > 0.0f;
   const float sl2 = ALIBI ? a.slopes[h] * RA_LOG2E : 0.0f;
 
-  // ---- tile movement: K and V global -> LDS (swizzled), positions via registers ----
-  // Slot p of a tile holds row p / CPR, physical chunk p % CPR, i.e. logical
-  // chunk (p % CPR) ^ swizzle(row). Each wave moves DMA_PER_WAVE x 64 slots.
-  auto dma_tile = [&](int buf, int kv0) {
+  // ---- tile movement ----
+  // Phase-1 copies are issued by the four waves of set 0 alone (DMA_SET0
+  // slots each, offsets precomputed); the other copies by all eight waves.
+  constexpr int DMA_SET0 = SLOTS / (4 * 64);
+  uint32_t dk_off[DMA_SET0], dv_off[DMA_SET0];
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int base = (wave * DMA_PER_WAVE + i) * 64;
-      const int p = base + lane;
-      const int r = p / CPR, ph = p % CPR;
-      const int grow = min(kv0 + r, Lkv - 1);
-      dma16(kh + (int64_t)grow * D + 8 * (ph ^ k_swz(r)), &Ks[buf][base]);
-      dma16(vh + (int64_t)grow * D + 8 * (ph ^ v_swz(r)), &Vs[buf][base]);
+  for (int i = 0; i < DMA_SET0; ++i) {
+    const int p = ((wave & 3) * DMA_SET0 + i) * 64 + lane;
+    const int r = p / CPR, ph = p % CPR;
+    dk_off[i] = (uint32_t)(r * D + 8 * (ph ^ k_swz(r))) * 2;
+    dv_off[i] = (uint32_t)(r * D + 8 * (ph ^ v_swz(r))) * 2;
+  }
+  auto dma_set0 = [&](int kbuf, int kv0k, bool do_k, int vbuf, int kv0v, bool do_v) {
+    // Only called for complete tiles (phase 1).
+    const char* kt = reinterpret_cast<const char*>(kh + (int64_t)kv0k * D);
+    const char* vt = reinterpret_cast<const char*>(vh + (int64_t)kv0v * D);
+#pragma unroll
+    for (int i = 0; i < DMA_SET0; ++i) {
+      const int base = ((wave & 3) * DMA_SET0 + i) * 64;
+      if (do_k) dma16(kt + dk_off[i], &Ks[kbuf][base]);
+      if (do_v) dma16(vt + dv_off[i], &Vs[vbuf][base]);
     }
   };
+  // All eight waves; rows past the end of the chunk are clamped to the last
+  // key (they are masked).
+  auto dma_all = [&](uint4* tile, const uint16_t* src, int kv0, bool is_v) {
+    const char* t = reinterpret_cast<const char*>(src + (int64_t)kv0 * D);
+    const int last = Lkv - 1 - kv0;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int base = (wave * DMA_PER_WAVE + i) * 64, p = base + lane, r = p / CPR, ph = p % CPR;
+      const int sw = is_v ? v_swz(r) : k_swz(r);
+      dma16(t + (uint32_t)(min(r, last) * D + 8 * (ph ^ sw)) * 2, &tile[base]);
+    }
+  };
+  auto dma_k = [&](int buf, int kv0) { dma_all(Ks[buf], kh, kv0, false); };
+  auto dma_v = [&](int buf, int kv0) { dma_all(Vs[buf], vh, kv0, true); };
   auto load_kp = [&](int kv0) { return tid < BN ? kpos[min(kv0 + tid, Lkv - 1)] : 0; };
   auto store_kp = [&](int buf, int kv0, int kpv) {
     if (tid < BN) {
@@ -203,16 +267,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(StepArgs a, int n
   float l_run = (row_ok && hf == 0) ? lh[row] : 0.0f;
   bool touched = false;
 
-  // S^T block sb (32 keys) of the tile in LDS buffer `buf`.
-  auto qk = [&](int buf, int sb) {
-    ra_f32x16 S = ra_f32x16{};
-    const int krow = 32 * sb + perm_row(l32);
-    const int sw = k_swz(krow);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) S = ra_mfma32(Ks[buf][krow * CPR + ((2 * kk + hf) ^ sw)], qf[kk], S);
-    return S;
-  };
-
   // V^T fragment for d tile dt and keys kb0 + 8*hf + 0..7 (two transposing reads).
   const int g16 = lane >> 4, j16 = lane & 15;
   auto v_frag = [&](int buf, int kb0, int dt) {
@@ -227,82 +281,73 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(StepArgs a, int n
     return make_uint4(r2[0].x, r2[0].y, r2[1].x, r2[1].y);
   };
 
-  // Scores of one 32-key block, in place (lane element e is key 32*sb +
-  // 16*(e/8) + 8*hf + e%8 of the tile); returns the lane's partial max.
-  // kFast leaves raw dot products (the scale is folded into the exponent
-  // later); the other modes leave base-2 scores without the per-row ALiBi
-  // constant; masked scores are -inf.
-  auto scores = [&](auto mode_tag, ra_f32x16& S, int buf, int sb, int kv0) {
-    constexpr int MODE = decltype(mode_tag)::value;
-    if constexpr (MODE == kAlibiLinear) {
-      const float4* kbv = reinterpret_cast<const float4*>(&kb[buf][32 * sb + 8 * hf]);
+  // Scores of the tile (two 32-key blocks, S[sb] element e = key 32*sb +
+  // 16*(e/8) + 8*hf + e%8) and its bf16 probabilities P[sb][8] for the next
+  // MFMA phase.
+  ra_f32x16 S[2];
+  uint32_t P[2][8];
+
+  // MFMA work of one step: O^T += V^T P^T for the previous tile (from
+  // Vs[vb]), then S^T = K Q^T for the current one (from Ks[kbuf]).
+  auto pv_mfma = [&](int vb) {
 #pragma unroll
-      for (int e8 = 0; e8 < 2; ++e8) {
-        const float4 x0 = kbv[4 * e8], x1 = kbv[4 * e8 + 1];
-        const float kv8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) S[8 * e8 + i] = fmaf(S[8 * e8 + i], c, kv8[i]);
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 pb = make_uint4(P[sb][4 * ks + 0], P[sb][4 * ks + 1], P[sb][4 * ks + 2], P[sb][4 * ks + 3]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt] = ra_mfma32(v_frag(vb, 32 * sb + 16 * ks, dt), pb, O[dt]);
       }
-    } else if constexpr (MODE == kExact) {
-      const int4* kpv = reinterpret_cast<const int4*>(&kp[buf][32 * sb + 8 * hf]);
+    }
+  };
+  auto qk_mfma = [&](int kbuf) {
 #pragma unroll
-      for (int e8 = 0; e8 < 2; ++e8) {
-        const int4 p0 = kpv[4 * e8], p1 = kpv[4 * e8 + 1];
-        const int kv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    for (int sb = 0; sb < 2; ++sb) {
+      ra_f32x16 acc = ra_f32x16{};
+      const int krow = 32 * sb + perm_row(l32);
+      const int sw = k_swz(krow);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int j = 32 * sb + 16 * e8 + 8 * hf + i;
-          float x = S[8 * e8 + i] * c;
-          if (ALIBI) x = fmaf(-sl2, (float)abs(my_pos - kv8[i]), x);
-          const bool vis = (kv0 + j < Lkv) && (!causal || kv8[i] <= my_pos);
-          S[8 * e8 + i] = vis ? x : -INFINITY;
+      for (int kk = 0; kk < KK; ++kk) acc = ra_mfma32(Ks[kbuf][krow * CPR + ((2 * kk + hf) ^ sw)], qf[kk], acc);
+      S[sb] = acc;
+    }
+  };
+
+  // Softmax of tile t in place: S -> P (bf16), lazy rescale of O and l.
+  auto softmax = [&](auto mode_tag, int buf, int kv0) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    float rowc = 0.0f;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      if constexpr (MODE == kAlibiLinear) {
+        const float4* kbv = reinterpret_cast<const float4*>(&kb[buf][32 * sb + 8 * hf]);
+#pragma unroll
+        for (int e8 = 0; e8 < 2; ++e8) {
+          const float4 x0 = kbv[4 * e8], x1 = kbv[4 * e8 + 1];
+          const float kv8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) S[sb][8 * e8 + i] = fmaf(S[sb][8 * e8 + i], c, kv8[i]);
+        }
+      } else if constexpr (MODE == kExact) {
+        const int4* kpv = reinterpret_cast<const int4*>(&kp[buf][32 * sb + 8 * hf]);
+#pragma unroll
+        for (int e8 = 0; e8 < 2; ++e8) {
+          const int4 p0 = kpv[4 * e8], p1 = kpv[4 * e8 + 1];
+          const int kv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int j = 32 * sb + 16 * e8 + 8 * hf + i;
+            float x = S[sb][8 * e8 + i] * c;
+            if (ALIBI) x = fmaf(-sl2, (float)abs(my_pos - kv8[i]), x);
+            const bool vis = (kv0 + j < Lkv) && (!causal || kv8[i] <= my_pos);
+            S[sb][8 * e8 + i] = vis ? x : -INFINITY;
+          }
         }
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, S[sb][e]);
     }
-    float t = S[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) t = fmaxf(t, S[e]);
-    return t;
-  };
-
-  // exp2, row sum and bf16 packing of one block, then O^T += V^T P^T.
-  auto pv = [&](auto mode_tag, const ra_f32x16& S, float off, int buf, int sb) {
-    constexpr int MODE = decltype(mode_tag)::value;
-    uint32_t P[8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      float x0, x1;
-      if constexpr (MODE == kFast) {
-        x0 = fmaf(S[e], c, off);
-        x1 = fmaf(S[e + 1], c, off);
-      } else {
-        x0 = S[e] + off;
-        x1 = S[e + 1] + off;
-      }
-      const float p0 = __builtin_amdgcn_exp2f(x0);
-      const float p1 = __builtin_amdgcn_exp2f(x1);
-      psum += p0 + p1;
-      P[e >> 1] = ra_pack_bf16(p0, p1);
-    }
-    l_run += psum;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint4 pb = make_uint4(P[4 * ks + 0], P[4 * ks + 1], P[4 * ks + 2], P[4 * ks + 3]);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt] = ra_mfma32(v_frag(buf, 32 * sb + 16 * ks, dt), pb, O[dt]);
-    }
-  };
-
-  // One 64-key tile: both score blocks, one row max, one lazy-rescale
-  // decision, then the two P.V products.
-  auto tile = [&](auto mode_tag, int buf, int kv0) {
-    constexpr int MODE = decltype(mode_tag)::value;
-    ra_f32x16 S0 = qk(buf, 0);
-    ra_f32x16 S1 = qk(buf, 1);
-    float tmax = fmaxf(scores(mode_tag, S0, buf, 0, kv0), scores(mode_tag, S1, buf, 1, kv0));
     tmax = fmaxf(tmax, ra_swap_halves(tmax));
-    float rowc = 0.0f;  // per-row additive term of kAlibiLinear
     if constexpr (MODE == kFast) {
       tmax *= c;
     } else if constexpr (MODE == kAlibiLinear) {
@@ -311,51 +356,169 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(StepArgs a, int n
       tmax += rowc;
     }
     m_max = fmaxf(m_max, tmax);
-    // Lazy rescale: only when a score exceeds the reference by more than 2^tau.
-    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kTau)) {
-      const float nref = fmaxf(m_ref, tmax);
-      const float alpha = nref == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - nref);
+    // Lazy rescale, branch-free: the reference only moves when a score
+    // exceeds it by more than 2^tau, so alpha is exactly 1 on almost every tile.
+    const float nref = tmax > m_ref + kTau ? fmaxf(m_ref, tmax) : m_ref;
+    const float alpha = nref == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - nref);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
-      l_run *= alpha;
-      m_ref = nref;
-    }
+    for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+    m_ref = nref;
     const float off = rowc - (m_ref == -INFINITY ? 0.0f : m_ref);
-    pv(mode_tag, S0, off, buf, 0);
-    pv(mode_tag, S1, off, buf, 1);
+    float psum = 0.0f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float x0, x1;
+        if constexpr (MODE == kFast) {
+          x0 = fmaf(S[sb][e], c, off);
+          x1 = fmaf(S[sb][e + 1], c, off);
+        } else {
+          x0 = S[sb][e] + off;
+          x1 = S[sb][e + 1] + off;
+        }
+        const float p0 = __builtin_amdgcn_exp2f(x0);
+        const float p1 = __builtin_amdgcn_exp2f(x1);
+        psum += p0 + p1;
+        P[sb][e >> 1] = ra_pack_bf16(p0, p1);
+      }
+    }
+    l_run = fmaf(l_run, alpha, psum);
+  };
+  constexpr int kUnmasked = ALIBI ? kAlibiLinear : kFast;
+
+  // Leading tiles that every row of the work-group sees in full (no mask, one
+  // code path for all eight waves), then the rest.
+  const int qmin_wg = a.q_pos[q0];
+  int T1 = 0;
+  if (fast_ok && (causal || !ALIBI)) {
+    T1 = Lkv / BN;  // complete tiles
+    if (causal) {
+      int lo = 0, hi = min(T1, T);  // first complete tile not entirely visible to qmin_wg
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (kpos[mid * BN + BN - 1] <= qmin_wg) lo = mid + 1; else hi = mid;
+      }
+      T1 = lo;
+    }
+    T1 = min(T1, T);
+  }
+
+  // A work-group barrier that the compiler may not move any instruction
+  // across, so that each set's MFMA and softmax phases stay where they are.
+  auto phase_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- prologue: tile 0 into LDS buffer 0 ----
-  dma_tile(0, 0);
-  store_kp(0, 0, load_kp(0));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Empty volatile asm that reads and rewrites the values a phase produces:
+  // the optimizer may then neither sink that phase's arithmetic past the
+  // barrier that follows it nor hoist the next phase's work above it.
+  auto pin_softmax = [&]() {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(P[sb][i]));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+v"(O[dt]));
+    asm volatile("" : "+v"(l_run), "+v"(m_ref), "+v"(m_max));
+  };
+  auto pin_mfma = [&]() {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) asm volatile("" : "+v"(S[sb]));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+v"(O[dt]));
+  };
 
-  for (int kv0 = 0, t = 0;; kv0 += BN, ++t) {
-    const int buf = t & 1;
-    const bool have_next = tile_live(kv0 + BN);
-    int kp_next = 0;
-    if (have_next) {  // that buffer was last read before the previous barrier
-      dma_tile(buf ^ 1, kv0 + BN);
-      kp_next = load_kp(kv0 + BN);
-    }
-
-    const int kfirst = uniform(kp[buf][0]);
-    const int klast = uniform(kp[buf][BN - 1]);
-    if (wave_active && !(causal && kfirst > qmax_w)) {
-      touched = true;
-      const bool masked = (kv0 + BN > Lkv) || (causal && klast > qmin_w) || !fast_ok;
-      if (masked || (ALIBI && !causal))
-        tile(std::integral_constant<int, kExact>{}, buf, kv0);
-      else if (ALIBI)
-        tile(std::integral_constant<int, kAlibiLinear>{}, buf, kv0);
-      else
-        tile(std::integral_constant<int, kFast>{}, buf, kv0);
-    }
-    if (!have_next) break;
-    store_kp(buf ^ 1, kv0 + BN, kp_next);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into the other buffer has landed
+  if (T1 > 0) {
+    // ---- phase 1: ping-pong. Both sets run the same instruction stream,
+    // "MFMA work of step t | barrier | softmax of tile t | barrier", set 1 one
+    // phase behind set 0 (one extra barrier at its start, set 0 one at its
+    // end), so on every SIMD one set's MFMAs overlap the other set's softmax.
+    // Step t's MFMA work is the P.V of tile t-1 and the QK of tile t. Set 0
+    // issues the copies at the start of its MFMA phase u: K(u+1) and V(u),
+    // waited for at the end of its following softmax phase.
+    touched = true;
+    dma_k(0, 0);
+    if constexpr (ALIBI) store_kp(0, 0, load_kp(0));
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    auto copies = [&](int u) {
+      if (set == 0) dma_set0((u + 1) & 1, (u + 1) * BN, u + 1 < T1, u & 1, u * BN, u < T1);
+    };
+    int kp_next = 0;
+    auto kp_fetch = [&](int u) {  // positions of tile u + 1 (ALiBi term)
+      if constexpr (ALIBI) if (u + 1 < T1) kp_next = load_kp((u + 1) * BN);
+    };
+    auto kp_publish = [&](int u) {
+      if constexpr (ALIBI) if (u + 1 < T1) store_kp((u + 1) & 1, (u + 1) * BN, kp_next);
+    };
+    if (set == 1) phase_barrier();
+    copies(0);
+    kp_fetch(0);
+    qk_mfma(0);
+    pin_mfma();
+    phase_barrier();
+#pragma clang loop unroll(disable)
+    for (int t = 0; t < T1; ++t) {
+      softmax(std::integral_constant<int, kUnmasked>{}, t & 1, t * BN);
+      pin_softmax();
+      if (set == 0) {
+        kp_publish(t);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      phase_barrier();
+      copies(t + 1);
+      kp_fetch(t + 1);
+      pv_mfma(t & 1);
+      qk_mfma((t + 1) & 1);  // the last one reads a stale tile and is discarded
+      // LDS fragment reads four MFMAs ahead of use.
+      interleave_mfma_reads<4 * DT, 2 * KK>();
+      pin_mfma();
+      phase_barrier();
+    }
+    if (set == 0) phase_barrier();
+  }
+
+  // ---- phase 2: the remaining tiles (diagonal, ragged, or ALiBi without the
+  // causal mask), one at a time with all eight waves in step; K, V of tile t
+  // in buffer (t - T1) & 1.
+  if (T1 < T) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    dma_k(0, T1 * BN);
+    dma_v(0, T1 * BN);
+    store_kp(0, T1 * BN, load_kp(T1 * BN));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma clang loop unroll(disable)
+    for (int t = T1; t < T; ++t) {
+      const int buf = (t - T1) & 1, kv0 = t * BN;
+      const bool have_next = t + 1 < T;
+      int kp_nx = 0;
+      if (have_next) {  // that buffer was last read before the previous barrier
+        dma_k(buf ^ 1, kv0 + BN);
+        dma_v(buf ^ 1, kv0 + BN);
+        kp_nx = load_kp(kv0 + BN);
+      }
+      const int kfirst = uniform(kp[buf][0]);
+      const int klast = uniform(kp[buf][BN - 1]);
+      if (wave_active && !(causal && kfirst > qmax_w)) {
+        touched = true;
+        qk_mfma(buf);
+        const bool masked = (kv0 + BN > Lkv) || (causal && klast > qmin_w) || !fast_ok;
+        if (masked || (ALIBI && !causal))
+          softmax(std::integral_constant<int, kExact>{}, buf, kv0);
+        else
+          softmax(std::integral_constant<int, kUnmasked>{}, buf, kv0);
+        pv_mfma(buf);
+      }
+      if (!have_next) break;
+      store_kp(buf ^ 1, kv0 + BN, kp_nx);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   if (!touched) return;
