@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
       if (tid < TROWS) {
         const int hq = item_head(it), q = min(item_q0(it) + tid, Lq - 1);
         const int64_t row = ((int64_t)b * a.heads_q + hq) * Lq + q;
-        r.lse = safe_lse2(a.lse[row]);
+        r.lse = a.lse[row];  // converted when stored: no use before the loop's end
         r.del = a.delta[row];
         r.qp = a.q_pos[q];
       }
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     };
     auto store_rows = [&](int buf, const RowVals& r) {
       if (tid < TROWS) {
-        lse_s[buf][tid] = r.lse;
+        lse_s[buf][tid] = safe_lse2(r.lse);
         del_s[buf][tid] = r.del;
         qp_s[buf][tid] = r.qp;
       }
@@ -181,9 +181,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
         nxt = load_rows(it + 1);
       }
       const int hq = item_head(it), q0 = item_q0(it);
-      const int qlast = a.q_pos[min(q0 + TROWS - 1, Lq - 1)];
+      // Positions of the item's first and last query row, from the LDS copy
+      // (kept off the vector-memory counter that the tile copies use).
+      const int qfirst = uniform_i(qp_s[buf][0]);
+      const int qlast = uniform_i(qp_s[buf][TROWS - 1]);
       if (wave_active && !(causal && qlast < kmin_w)) {
-        const bool diag = (q0 + TROWS > Lq) || (causal && a.q_pos[q0] < kmax_w) || ALIBI;
+        const bool diag = (q0 + TROWS > Lq) || (causal && qfirst < kmax_w) || ALIBI;
         const float sl2 = ALIBI ? a.slopes[hq] * RA_LOG2E : 0.0f;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -335,7 +338,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
 #pragma clang loop unroll(disable)
   for (int kv0 = 0, t = 0;; kv0 += TROWS, ++t) {
     const int buf = t & 1;
-    const bool have_next = tile_live(kv0 + TROWS);
+    // The next tile is copied whenever it exists; whether any query of the
+    // work-group sees it is decided once its positions are in LDS.
+    const bool have_next = kv0 + TROWS < Lkv;
     int kp_next = 0;
     if (have_next) {
       dma_tile(Ks[buf ^ 1], kh, kv0 + TROWS, Lkv, wave, lane, off);
@@ -396,6 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
     if (tid < TROWS) kp[buf ^ 1][tid] = kp_next;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (causal && uniform_i(kp[buf ^ 1][0]) > qmax_wg) break;  // keys past the last query
   }
 
   if (!touched || !row_ok) return;

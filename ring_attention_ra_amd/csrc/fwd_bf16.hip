@@ -34,14 +34,18 @@
 //    of the previous tile and the QK product of the current one; its LDS
 //    fragment reads run four MFMAs ahead of use. Set 0 issues the copies of
 //    the next K and current V tile at the start of its MFMA phase and waits
-//    for them before the next barrier. Empty volatile asm statements pin each
+//    for them before the barrier that ends its next softmax phase; the copies
+//    are invisible to the compiler's wait insertion, so the fragment reads of
+//    the other buffers go ahead while they fly. Empty volatile asm statements pin each
 //    phase's results and scheduling barriers keep the compiler from moving
 //    work across the work-group barriers. The remaining tiles (diagonal,
 //    ragged, or ALiBi without the causal mask) follow one at a time with all
 //    waves in step and per-element masks where needed.
 //  * The output is rescaled lazily: exponents are taken against a reference
 //    max that is raised (and O, l rescaled) only when a score exceeds it by
-//    more than 2^8; P then stays below 2^8, well inside bf16 / fp32 range. The
+//    more than 2^8; P then stays below 2^8, well inside bf16 / fp32 range.
+//    Over the fully visible tiles the multiply of O is skipped when no lane of
+//    the wave moved its reference (the common case after the first tiles). The
 //    true running max is tracked alongside, and the state is renormalised to
 //    it once before it is written, so memory holds exactly m = max s,
 //    l = sum exp(s - m), o_acc = sum exp(s - m) v.
@@ -58,7 +62,7 @@
 //    a wave spread over the banks.
 #include <type_traits>
 
-#include "ra_internal.h"
+#include "tile_common.h"
 
 namespace ra {
 namespace {
@@ -71,44 +75,9 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
 
 enum TileMode { kFast = 0, kAlibiLinear = 1, kExact = 2 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((ext_vector_type(4))) short ra_s16x4;
-
-// K-operand row permutation: swap bits 2 and 3 of a row index in [0, 32).
-__device__ __forceinline__ int perm_row(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
 // 16-byte chunk swizzles of the K and V rows in LDS.
 __device__ __forceinline__ int k_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, float a0, float a1,
-                                            float a2, float a3) {
-  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-  u32x4 v = {__float_as_uint(a0), __float_as_uint(a1), __float_as_uint(a2), __float_as_uint(a3)};
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
-}
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane.
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (lds_void*)lds_base, 16, 0, 0);
-}
-// Transposing LDS read, 4 bf16 per lane (see the header comment).
-__device__ __forceinline__ uint2 lds_tr4(const void* p) {
-  const ra_s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) ra_s16x4*)((__attribute__((address_space(3))) char*)(p)));
-  return __builtin_bit_cast(uint2, r);
-}
 
 // Scheduling pattern of one MFMA phase: NPV P.V products (two transposing LDS
 // reads each) followed by NQK QK products (one LDS read each). The reads of
@@ -158,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   const int hk = h / (a.heads_q / a.heads_kv);
 
   const int tid = threadIdx.x;
-  const int wave = uniform(tid >> 6), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = uniform_i(tid >> 6), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int set = wave >> 2;  // two sets of 4 waves, half a tile apart
   const int q0 = qt * BM, q0w = q0 + wave * 32;
   const int row = q0w + l32;
@@ -313,8 +282,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   };
 
   // Softmax of tile t in place: S -> P (bf16), lazy rescale of O and l.
-  auto softmax = [&](auto mode_tag, int buf, int kv0) {
+  auto softmax = [&](auto mode_tag, int buf, int kv0, auto cond_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool COND = decltype(cond_tag)::value;
     float rowc = 0.0f;
     float tmax = -INFINITY;
 #pragma unroll
@@ -352,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       tmax *= c;
     } else if constexpr (MODE == kAlibiLinear) {
       // bias = -slope*(pos_q - pos_k) = slope*(pos_k - base) - slope*(pos_q - base)
-      rowc = -sl2 * (float)(my_pos - uniform(kpos[kv0]));
+      rowc = -sl2 * (float)(my_pos - uniform_i(kpos[kv0]));
       tmax += rowc;
     }
     m_max = fmaxf(m_max, tmax);
@@ -360,8 +330,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     // exceeds it by more than 2^tau, so alpha is exactly 1 on almost every tile.
     const float nref = tmax > m_ref + kTau ? fmaxf(m_ref, tmax) : m_ref;
     const float alpha = nref == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - nref);
+    // Phase 1 skips the multiply when no lane of the wave moved its
+    // reference; the per-tile loop of phase 2 keeps it branch-free.
+    if (!COND || __builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+    }
     m_ref = nref;
     const float off = rowc - (m_ref == -INFINITY ? 0.0f : m_ref);
     float psum = 0.0f;
@@ -462,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     phase_barrier();
 #pragma clang loop unroll(disable)
     for (int t = 0; t < T1; ++t) {
-      softmax(std::integral_constant<int, kUnmasked>{}, t & 1, t * BN);
+      softmax(std::integral_constant<int, kUnmasked>{}, t & 1, t * BN, std::true_type{});
       pin_softmax();
       if (set == 0) {
         kp_publish(t);
@@ -502,16 +476,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
         dma_v(buf ^ 1, kv0 + BN);
         kp_nx = load_kp(kv0 + BN);
       }
-      const int kfirst = uniform(kp[buf][0]);
-      const int klast = uniform(kp[buf][BN - 1]);
+      const int kfirst = uniform_i(kp[buf][0]);
+      const int klast = uniform_i(kp[buf][BN - 1]);
       if (wave_active && !(causal && kfirst > qmax_w)) {
         touched = true;
         qk_mfma(buf);
         const bool masked = (kv0 + BN > Lkv) || (causal && klast > qmin_w) || !fast_ok;
         if (masked || (ALIBI && !causal))
-          softmax(std::integral_constant<int, kExact>{}, buf, kv0);
+          softmax(std::integral_constant<int, kExact>{}, buf, kv0, std::false_type{});
         else
-          softmax(std::integral_constant<int, kUnmasked>{}, buf, kv0);
+          softmax(std::integral_constant<int, kUnmasked>{}, buf, kv0, std::false_type{});
         pv_mfma(buf);
       }
       if (!have_next) break;

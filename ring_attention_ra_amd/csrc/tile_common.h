@@ -44,10 +44,16 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane.
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane
+// (lds_base is wave-uniform). Issued from inline assembly so that the compiler
+// does not track the copy: it would otherwise wait for every copy in flight
+// before the next LDS read, including reads of the other buffer. Callers wait
+// for completion explicitly (s_waitcnt vmcnt(0)) before the barrier that
+// publishes the tile.
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (ra_lds_void*)lds_base, 16, 0, 0);
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ra_lds_void*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la)
+               : "m0");
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane
