@@ -10,8 +10,8 @@
 //
 // How it maps onto the MI355X:
 //  * One 512-thread work-group (8 waves) owns 256 query rows of one head;
-//    each wave owns 32 rows. K/V stream through a double-buffered LDS tile of
-//    64 keys, moved global -> LDS by the DMA path (global_load_lds_dwordx4, no
+//    each wave owns 32 rows. K/V stream through LDS in tiles of 64 keys,
+//    moved global -> LDS by the DMA path (global_load_lds_dwordx4, no
 //    register staging). Rows past the end of the chunk are clamped to the
 //    last key and masked.
 //  * The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so every
@@ -32,15 +32,18 @@
 //    one phase behind set 0, so on each SIMD one wave's matrix products
 //    overlap the other wave's exponentials. An MFMA phase is the P.V product
 //    of the previous tile and the QK product of the current one; its LDS
-//    fragment reads run four MFMAs ahead of use. Set 0 issues the copies of
-//    the next K and current V tile at the start of its MFMA phase and waits
-//    for them before the barrier that ends its next softmax phase; the copies
-//    are invisible to the compiler's wait insertion, so the fragment reads of
-//    the other buffers go ahead while they fly. Empty volatile asm statements pin each
-//    phase's results and scheduling barriers keep the compiler from moving
-//    work across the work-group barriers. The remaining tiles (diagonal,
-//    ragged, or ALiBi without the causal mask) follow one at a time with all
-//    waves in step and per-element masks where needed.
+//    fragment reads run four MFMAs ahead of use. K and V have three LDS
+//    buffers each: at the end of its MFMA phase for tile t every wave copies
+//    its share of K(t+3) and V(t+2) into the buffers that tiles t and t-1
+//    leave, and waits for its previous step's copies before the barrier, so
+//    a copy has two phases to land. The copies are issued from inline
+//    assembly, invisible to the compiler's wait insertion, so fragment reads
+//    of the other buffers go ahead while they fly. Empty volatile asm
+//    statements pin each phase's results and scheduling barriers keep the
+//    compiler from moving work across the work-group barriers. The
+//    remaining tiles (diagonal, ragged, or ALiBi without the causal mask)
+//    follow one at a time with all waves in step, double-buffered, with
+//    per-element masks where needed.
 //  * The output is rescaled lazily: exponents are taken against a reference
 //    max that is raised (and O, l rescaled) only when a score exceeds it by
 //    more than 2^8; P then stays below 2^8, well inside bf16 / fp32 range.
@@ -74,6 +77,13 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
 
 enum TileMode { kFast = 0, kAlibiLinear = 1, kExact = 2 };
+
+// 4 bytes per lane from global memory into LDS at lds_base + 4*lane (issued
+// like dma16: untracked by the compiler, awaited explicitly).
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ra_lds_void*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(la) : "m0");
+}
 
 // 16-byte chunk swizzles of the K and V rows in LDS.
 __device__ __forceinline__ int k_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
@@ -109,10 +119,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   constexpr int SLOTS = BN * CPR;       // 16-byte slots in a K (or V) tile
   constexpr int DMA_PER_WAVE = SLOTS / (kWaves * 64);
 
-  __shared__ uint4 Ks[2][SLOTS];
-  __shared__ uint4 Vs[2][SLOTS];
-  __shared__ __align__(16) int kp[2][BN];
-  __shared__ __align__(16) float kb[ALIBI ? 2 : 1][BN];
+  __shared__ uint4 Ks[3][SLOTS];
+  __shared__ uint4 Vs[3][SLOTS];
+  __shared__ __align__(16) int kp[3][BN];
+  __shared__ __align__(16) float kb[ALIBI ? 3 : 1][BN];
+  __shared__ int kbase[3];  // position of the first key of the tile in kb[]
 
   const int Lq = a.len_q, Lkv = a.len_kv;
   const int BH = a.batch * a.heads_q;
@@ -166,27 +177,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   const float sl2 = ALIBI ? a.slopes[h] * RA_LOG2E : 0.0f;
 
   // ---- tile movement ----
-  // Phase-1 copies are issued by the four waves of set 0 alone (DMA_SET0
-  // slots each, offsets precomputed); the other copies by all eight waves.
-  constexpr int DMA_SET0 = SLOTS / (4 * 64);
-  uint32_t dk_off[DMA_SET0], dv_off[DMA_SET0];
+  // Phase-1 copies: every wave moves DMA_PER_WAVE 16-byte slots of a K
+  // tile and of a V tile (offsets precomputed).
+  uint32_t dk_off[DMA_PER_WAVE], dv_off[DMA_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < DMA_SET0; ++i) {
-    const int p = ((wave & 3) * DMA_SET0 + i) * 64 + lane;
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int p = (wave * DMA_PER_WAVE + i) * 64 + lane;
     const int r = p / CPR, ph = p % CPR;
     dk_off[i] = (uint32_t)(r * D + 8 * (ph ^ k_swz(r))) * 2;
     dv_off[i] = (uint32_t)(r * D + 8 * (ph ^ v_swz(r))) * 2;
   }
-  auto dma_set0 = [&](int kbuf, int kv0k, bool do_k, int vbuf, int kv0v, bool do_v) {
-    // Only called for complete tiles (phase 1).
+  auto dma_p1 = [&](int kbuf, int kv0k, int vbuf, int kv0v) {  // complete tiles only
     const char* kt = reinterpret_cast<const char*>(kh + (int64_t)kv0k * D);
     const char* vt = reinterpret_cast<const char*>(vh + (int64_t)kv0v * D);
 #pragma unroll
-    for (int i = 0; i < DMA_SET0; ++i) {
-      const int base = ((wave & 3) * DMA_SET0 + i) * 64;
-      if (do_k) dma16(kt + dk_off[i], &Ks[kbuf][base]);
-      if (do_v) dma16(vt + dv_off[i], &Vs[vbuf][base]);
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int base = (wave * DMA_PER_WAVE + i) * 64;
+      dma16(kt + dk_off[i], &Ks[kbuf][base]);
+      dma16(vt + dv_off[i], &Vs[vbuf][base]);
     }
+    // ALiBi: wave 0 also copies the key positions of the K tile.
+    if constexpr (ALIBI) if (wave == 0) dma4(kpos + kv0k + lane, &kp[kbuf][0]);
   };
   // All eight waves; rows past the end of the chunk are clamped to the last
   // key (they are masked).
@@ -206,7 +217,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   auto store_kp = [&](int buf, int kv0, int kpv) {
     if (tid < BN) {
       kp[buf][tid] = kpv;
-      if constexpr (ALIBI) kb[buf][tid] = sl2 * (float)(kpv - kpos[kv0]);
+      if constexpr (ALIBI) {
+        const int k0 = kpos[kv0];
+        kb[buf][tid] = sl2 * (float)(kpv - k0);
+        if (tid == 0) kbase[buf] = k0;
+      }
     }
   };
 
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       tmax *= c;
     } else if constexpr (MODE == kAlibiLinear) {
       // bias = -slope*(pos_q - pos_k) = slope*(pos_k - base) - slope*(pos_q - base)
-      rowc = -sl2 * (float)(my_pos - uniform_i(kpos[kv0]));
+      rowc = -sl2 * (float)(my_pos - uniform_i(kbase[buf]));
       tmax += rowc;
     }
     m_max = fmaxf(m_max, tmax);
@@ -414,43 +429,58 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     // issues the copies at the start of its MFMA phase u: K(u+1) and V(u),
     // waited for at the end of its following softmax phase.
     touched = true;
+    // Three K and three V buffers; tile u lives in buffer u % 3. K(0..2) and
+    // V(0..1) are loaded up front (clamped to the last phase-1 tile).
     dma_k(0, 0);
-    if constexpr (ALIBI) store_kp(0, 0, load_kp(0));
+    dma_k(1, min(1, T1 - 1) * BN);
+    dma_k(2, min(2, T1 - 1) * BN);
+    dma_v(0, 0);
+    dma_v(1, min(1, T1 - 1) * BN);
+    if constexpr (ALIBI) {
+      store_kp(0, 0, load_kp(0));
+      store_kp(1, min(1, T1 - 1) * BN, load_kp(min(1, T1 - 1) * BN));
+      store_kp(2, min(2, T1 - 1) * BN, load_kp(min(2, T1 - 1) * BN));
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    auto copies = [&](int u) {
-      if (set == 0) dma_set0((u + 1) & 1, (u + 1) * BN, u + 1 < T1, u & 1, u * BN, u < T1);
-    };
-    int kp_next = 0;
-    auto kp_fetch = [&](int u) {  // positions of tile u + 1 (ALiBi term)
-      if constexpr (ALIBI) if (u + 1 < T1) kp_next = load_kp((u + 1) * BN);
-    };
-    auto kp_publish = [&](int u) {
-      if constexpr (ALIBI) if (u + 1 < T1) store_kp((u + 1) & 1, (u + 1) * BN, kp_next);
-    };
     if (set == 1) phase_barrier();
-    copies(0);
-    kp_fetch(0);
     qk_mfma(0);
     pin_mfma();
     phase_barrier();
+    // Buffers of tiles t, t+1, t+2 (rotating).
+    int b0 = 0, b1 = 1, b2 = 2;
 #pragma clang loop unroll(disable)
     for (int t = 0; t < T1; ++t) {
-      softmax(std::integral_constant<int, kUnmasked>{}, t & 1, t * BN, std::true_type{});
+      softmax(std::integral_constant<int, kUnmasked>{}, b0, t * BN, std::true_type{});
       pin_softmax();
-      if (set == 0) {
-        kp_publish(t);
-        __builtin_amdgcn_s_waitcnt(0);
-      }
       phase_barrier();
-      copies(t + 1);
-      kp_fetch(t + 1);
-      pv_mfma(t & 1);
-      qk_mfma((t + 1) & 1);  // the last one reads a stale tile and is discarded
+      pv_mfma(b0);
+      qk_mfma(b1);  // the last one reads a stale tile and is discarded
       // LDS fragment reads four MFMAs ahead of use.
       interleave_mfma_reads<4 * DT, 2 * KK>();
+      // Copies two tiles ahead, issued after this phase's fragment reads:
+      // K(t+3) into the buffer K(t) leaves, V(t+2) into the one V(t-1) left
+      // (clamped to the last phase-1 tile). Every reader of those buffers
+      // has passed a barrier since. This wave's copies of the previous step
+      // must land before the barrier; this step's may stay in flight.
+      dma_p1(b0, min(t + 3, T1 - 1) * BN, b2, min(t + 2, T1 - 1) * BN);
       pin_mfma();
+      // s_waitcnt vmcnt(n), n = this step's copies (expcnt and lgkmcnt fields
+      // at their maximum: no wait; vmcnt in bits 3:0).
+      if (ALIBI && wave == 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_PER_WAVE + 1));
+        // Key positions of tile t+2 have landed: its ALiBi terms.
+        const int kpv = kp[b2][lane], k0 = kp[b2][0];
+        kb[b2][lane] = sl2 * (float)(kpv - k0);
+        if (lane == 0) kbase[b2] = k0;
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_PER_WAVE));
+      }
       phase_barrier();
+      const int bn = b0;
+      b0 = b1;
+      b1 = b2;
+      b2 = bn;
     }
     if (set == 0) phase_barrier();
   }
