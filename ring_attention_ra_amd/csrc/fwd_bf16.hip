@@ -30,9 +30,11 @@
 //    SIMD): over the tiles that every row of the work-group sees in full,
 //    both sets run "MFMA phase | barrier | softmax phase | barrier" with set 1
 //    one phase behind set 0, so on each SIMD one wave's matrix products
-//    overlap the other wave's exponentials. An MFMA phase is the P.V product
-//    of the previous tile and the QK product of the current one; its LDS
-//    fragment reads run four MFMAs ahead of use. K and V have three LDS
+//    overlap the other wave's exponentials. An MFMA phase is the QK product
+//    of the next tile and the P.V product of the current one; its LDS
+//    fragment reads run four MFMAs ahead of use, and the wave raises its
+//    issue priority for the phase so that its MFMAs and reads are not held
+//    behind the other wave's VALU work. K and V have three LDS
 //    buffers each: at the end of its MFMA phase for tile t every wave copies
 //    its share of K(t+3) and V(t+2) into the buffers that tiles t and t-1
 //    leave, and waits for its previous step's copies before the barrier, so
@@ -89,25 +91,24 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
 __device__ __forceinline__ int k_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
 
-// Scheduling pattern of one MFMA phase: NPV P.V products (two transposing LDS
-// reads each) followed by NQK QK products (one LDS read each). The reads of
+// Scheduling pattern of one MFMA phase: NQK QK products (one LDS read each)
+// followed by NPV P.V products (two transposing LDS reads each). The reads of
 // the first four products go first; after product i come the reads of
 // product i + 4.
-template <int NPV, int NQK, int I>
-__device__ __forceinline__ void interleave_step() {
+template <int NQK, int NPV, int I>
+__device__ __forceinline__ void interleave_qk_step() {
   if constexpr (I < NPV + NQK) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     if constexpr (I + 4 < NPV + NQK) {
-      __builtin_amdgcn_sched_group_barrier(0x100, (I + 4 < NPV ? 2 : 1), 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, (I + 4 < NQK ? 1 : 2), 0);  // LDS reads
     }
-    interleave_step<NPV, NQK, I + 1>();
+    interleave_qk_step<NQK, NPV, I + 1>();
   }
 }
-template <int NPV, int NQK>
-__device__ __forceinline__ void interleave_mfma_reads() {
-  constexpr int first = (NPV >= 4 ? 8 : 2 * NPV + (4 - NPV));
-  __builtin_amdgcn_sched_group_barrier(0x100, first, 0);
-  interleave_step<NPV, NQK, 0>();
+template <int NQK, int NPV>
+__device__ __forceinline__ void interleave_qk_first() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of QK products 0..3
+  interleave_qk_step<NQK, NPV, 0>();
 }
 
 template <int D, bool ALIBI>
@@ -454,10 +455,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       softmax(std::integral_constant<int, kUnmasked>{}, b0, t * BN, std::true_type{});
       pin_softmax();
       phase_barrier();
-      pv_mfma(b0);
+      __builtin_amdgcn_s_setprio(1);
       qk_mfma(b1);  // the last one reads a stale tile and is discarded
+      pv_mfma(b0);
       // LDS fragment reads four MFMAs ahead of use.
-      interleave_mfma_reads<4 * DT, 2 * KK>();
+      interleave_qk_first<2 * KK, 4 * DT>();
       // Copies two tiles ahead, issued after this phase's fragment reads:
       // K(t+3) into the buffer K(t) leaves, V(t+2) into the one V(t-1) left
       // (clamped to the last phase-1 tile). Every reader of those buffers
@@ -465,6 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       // must land before the barrier; this step's may stay in flight.
       dma_p1(b0, min(t + 3, T1 - 1) * BN, b2, min(t + 2, T1 - 1) * BN);
       pin_mfma();
+      __builtin_amdgcn_s_setprio(0);
       // s_waitcnt vmcnt(n), n = this step's copies (expcnt and lgkmcnt fields
       // at their maximum: no wait; vmcnt in bits 3:0).
       if (ALIBI && wave == 0) {
