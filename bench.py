@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--workload", default=str(configs.HEADLINE.index),
                     help="workload index (1-5) or name; default: the 128K zig-zag share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows in the CPU-baseline sample")
     ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-baseline sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fwd_bf16_128k_zigzag_traffic.json"),
                     help="JSON with counter-measured HBM bytes per step-kernel launch; used only when it was "
