@@ -16,7 +16,10 @@
 //    dP = dO V^T run with the query rows as the MFMA A operand (rows permuted
 //    so that each lane holds one key and 8 consecutive queries per k-step),
 //    which makes P^T and dS^T ready-made A operands for dV += P^T dO and
-//    dK += dS^T Q; dO and Q are read with the transposing LDS read.
+//    dK += dS^T Q; dO and Q are read with the transposing LDS read. The
+//    accumulators need one wave per SIMD; on unmasked tiles the two 32-query
+//    halves of a tile are software-pipelined so that one half's exponentials
+//    run between the other half's matrix products.
 //  * bwd_dq_kernel: a work-group owns 128 queries (4 waves x 32) and walks the
 //    key tiles, like the forward step: S^T = K Q^T and dP^T = V dO^T (Q and dO
 //    fragments in registers), then dQ^T += K^T dS^T with K^T from the
@@ -166,6 +169,175 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
       }
     };
 
+    // An item with masked elements (across the diagonal, ragged, or ALiBi):
+    // one 32-query block after the other, masked per element.
+    auto masked_item = [&](int buf, int q0, int hq) {
+      const float sl2 = ALIBI ? a.slopes[hq] * RA_LOG2E : 0.0f;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        ra_f32x16 S = ra_f32x16{}, dP = ra_f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          S = ra_mfma32(tile_row_frag(Qs[buf], 32 * qb, kk, lane), kf[kk], S);
+          dP = ra_mfma32(tile_row_frag(Os[buf], 32 * qb, kk, lane), vf[kk], dP);
+        }
+        // Lane element e: key `key`, query row 32*qb + 16*(e/8) + 8*hf + e%8.
+        uint32_t Pw[8], Dw[8];
+#pragma unroll
+        for (int e8 = 0; e8 < 2; ++e8) {
+          const int r0 = 32 * qb + 16 * e8 + 8 * hf;
+          const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[buf][r0]);
+          const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[buf][r0 + 4]);
+          const float4 d0 = *reinterpret_cast<const float4*>(&del_s[buf][r0]);
+          const float4 d1 = *reinterpret_cast<const float4*>(&del_s[buf][r0 + 4]);
+          const int4 p0 = *reinterpret_cast<const int4*>(&qp_s[buf][r0]);
+          const int4 p1 = *reinterpret_cast<const int4*>(&qp_s[buf][r0 + 4]);
+          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+          const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+          const int qv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float x = fmaf(S[8 * e8 + i], c, -lv[i]);
+            if (ALIBI) x = fmaf(-sl2, (float)abs(qv[i] - my_kpos), x);
+            const bool vis = (q0 + r0 + i < Lq) && key_ok && (!causal || my_kpos <= qv[i]);
+            p[i] = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            Pw[4 * e8 + i / 2] = ra_pack_bf16(p[i], p[i + 1]);
+            Dw[4 * e8 + i / 2] =
+                ra_pack_bf16(p[i] * (dP[8 * e8 + i] - dv[i]), p[i + 1] * (dP[8 * e8 + i + 1] - dv[i + 1]));
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint4 pa = make_uint4(Pw[4 * ks], Pw[4 * ks + 1], Pw[4 * ks + 2], Pw[4 * ks + 3]);
+          const uint4 da = make_uint4(Dw[4 * ks], Dw[4 * ks + 1], Dw[4 * ks + 2], Dw[4 * ks + 3]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            dV[dt] = ra_mfma32(pa, tile_col_frag(Os[buf], 32 * qb + 16 * ks, 32 * dt, lane), dV[dt]);
+            dK[dt] = ra_mfma32(da, tile_col_frag(Qs[buf], 32 * qb + 16 * ks, 32 * dt, lane), dK[dt]);
+          }
+        }
+      }
+    };
+
+    // Per-lane parts of the fragment addresses. A row fragment of rows
+    // r0 + perm_row(lane%32), k-step kk sits at byte r0*256 + (kk/4)*128 +
+    // rofs[kk%4]; a column fragment (tile_col_frag) of rows r0, columns 32*dt
+    // at r0*256 + (dt/2)*128 + cofs[half][dt%2] (the swizzle of a row depends
+    // only on its offset inside a 16-row group, so r0 and the high column bit
+    // add as constants).
+    int rofs[4], cofs[2][2];
+    {
+      const int pr = perm_row(l32), g = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) rofs[m] = pr * 256 + ((2 * m + hf) ^ tile_swz(pr)) * 16;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int rl = 8 * hf + 4 * half + (j >> 2), x = 2 * g + ((j & 3) >> 1);
+          cofs[half][db] = rl * 256 + ((4 * db + x) ^ tile_swz(rl)) * 16 + 8 * (j & 1);
+        }
+    }
+    auto row_frag = [&](const uint4* tile, int r0, int kk) {
+      return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + r0 * 256 + (kk >> 2) * 128 +
+                                             rofs[kk & 3]);
+    };
+    auto col_frag = [&](const uint4* tile, int r0, int dt) {
+      const char* t = reinterpret_cast<const char*>(tile) + r0 * 256 + (dt >> 1) * 128;
+      const uint2 a0 = lds_tr4(t + cofs[0][dt & 1]);
+      const uint2 a1 = lds_tr4(t + cofs[1][dt & 1]);
+      return make_uint4(a0.x, a0.y, a1.x, a1.y);
+    };
+    // An item every (query, key) pair of which is visible: no masks. With
+    // one wave per SIMD the overlap of matrix and vector work has to come
+    // from within the wave, so the code runs as
+    //   S, dP (block 0) | S, dP (block 1), P and dS of block 0 in between
+    //   | dV, dK (block 0), P and dS of block 1 in between | dV, dK (block 1)
+    // with a scheduling fence after every step, and fragments are read a few
+    // steps ahead of their products.
+    auto fast_item = [&](int buf) {
+      auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+      ra_f32x16 S[2], dP[2];
+      uint32_t Pw[2][8], Dw[2][8];
+      float lv[16], dv[16];  // lse, delta of the lane's 16 rows of one block
+      auto load_lsedel = [&](int qb) {
+#pragma unroll
+        for (int e8 = 0; e8 < 2; ++e8) {
+          const int r0 = 32 * qb + 16 * e8 + 8 * hf;
+          const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[buf][r0]);
+          const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[buf][r0 + 4]);
+          const float4 d0 = *reinterpret_cast<const float4*>(&del_s[buf][r0]);
+          const float4 d1 = *reinterpret_cast<const float4*>(&del_s[buf][r0 + 4]);
+          lv[8 * e8 + 0] = l0.x; lv[8 * e8 + 1] = l0.y; lv[8 * e8 + 2] = l0.z; lv[8 * e8 + 3] = l0.w;
+          lv[8 * e8 + 4] = l1.x; lv[8 * e8 + 5] = l1.y; lv[8 * e8 + 6] = l1.z; lv[8 * e8 + 7] = l1.w;
+          dv[8 * e8 + 0] = d0.x; dv[8 * e8 + 1] = d0.y; dv[8 * e8 + 2] = d0.z; dv[8 * e8 + 3] = d0.w;
+          dv[8 * e8 + 4] = d1.x; dv[8 * e8 + 5] = d1.y; dv[8 * e8 + 6] = d1.z; dv[8 * e8 + 7] = d1.w;
+        }
+      };
+      // VALU work of block qb for elements 2*j, 2*j + 1: P, dS, both packed.
+      auto valu = [&](int qb, int j) {
+        const int e = 2 * j;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[qb][e], c, -lv[e]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[qb][e + 1], c, -lv[e + 1]));
+        Pw[qb][j] = ra_pack_bf16(p0, p1);
+        Dw[qb][j] = ra_pack_bf16(p0 * (dP[qb][e] - dv[e]), p1 * (dP[qb][e + 1] - dv[e + 1]));
+      };
+      // S, dP of block qb; row fragments read LA k-steps ahead; extra(kk)
+      // runs between the k-steps.
+      constexpr int LA = 3;
+      auto sdp = [&](int qb, auto extra) {
+        uint4 qa[LA + 1], oa[LA + 1];
+#pragma unroll
+        for (int kk = 0; kk < LA; ++kk) {
+          qa[kk] = row_frag(Qs[buf], 32 * qb, kk);
+          oa[kk] = row_frag(Os[buf], 32 * qb, kk);
+        }
+        S[qb] = ra_f32x16{};
+        dP[qb] = ra_f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + LA < KK) {
+            qa[(kk + LA) % (LA + 1)] = row_frag(Qs[buf], 32 * qb, kk + LA);
+            oa[(kk + LA) % (LA + 1)] = row_frag(Os[buf], 32 * qb, kk + LA);
+          }
+          S[qb] = ra_mfma32(qa[kk % (LA + 1)], kf[kk], S[qb]);
+          dP[qb] = ra_mfma32(oa[kk % (LA + 1)], vf[kk], dP[qb]);
+          extra(kk);
+          fence();
+        }
+      };
+      // dV, dK of block qb; column fragments read one step ahead.
+      auto dvdk = [&](int qb, bool with_valu) {
+        uint4 ob[2], qbf[2];
+        ob[0] = col_frag(Os[buf], 32 * qb, 0);
+        qbf[0] = col_frag(Qs[buf], 32 * qb, 0);
+#pragma unroll
+        for (int st = 0; st < 2 * DT; ++st) {  // st = ks * DT + dt
+          const int ks = st / DT, dt = st % DT;
+          if (st + 1 < 2 * DT) {
+            const int ks1 = (st + 1) / DT, dt1 = (st + 1) % DT;
+            ob[(st + 1) & 1] = col_frag(Os[buf], 32 * qb + 16 * ks1, dt1);
+            qbf[(st + 1) & 1] = col_frag(Qs[buf], 32 * qb + 16 * ks1, dt1);
+          }
+          const uint4 pa = make_uint4(Pw[qb][4 * ks], Pw[qb][4 * ks + 1], Pw[qb][4 * ks + 2], Pw[qb][4 * ks + 3]);
+          const uint4 da = make_uint4(Dw[qb][4 * ks], Dw[qb][4 * ks + 1], Dw[qb][4 * ks + 2], Dw[qb][4 * ks + 3]);
+          dV[dt] = ra_mfma32(pa, ob[st & 1], dV[dt]);
+          dK[dt] = ra_mfma32(da, qbf[st & 1], dK[dt]);
+          if (with_valu) valu(1, st);
+          fence();
+        }
+      };
+      load_lsedel(0);
+      sdp(0, [](int) {});
+      sdp(1, [&](int kk) { valu(0, kk); });
+      load_lsedel(1);
+      dvdk(0, true);
+      dvdk(1, false);
+    };
     load_item(0, 0);
     store_rows(0, load_rows(0));
     __builtin_amdgcn_s_waitcnt(0);
@@ -187,60 +359,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
       const int qlast = uniform_i(qp_s[buf][TROWS - 1]);
       if (wave_active && !(causal && qlast < kmin_w)) {
         const bool diag = (q0 + TROWS > Lq) || (causal && qfirst < kmax_w) || ALIBI;
-        const float sl2 = ALIBI ? a.slopes[hq] * RA_LOG2E : 0.0f;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          ra_f32x16 S = ra_f32x16{}, dP = ra_f32x16{};
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            S = ra_mfma32(tile_row_frag(Qs[buf], 32 * qb, kk, lane), kf[kk], S);
-            dP = ra_mfma32(tile_row_frag(Os[buf], 32 * qb, kk, lane), vf[kk], dP);
-          }
-          // Lane element e: key `key`, query row 32*qb + 16*(e/8) + 8*hf + e%8.
-          uint32_t Pw[8], Dw[8];
-#pragma unroll
-          for (int e8 = 0; e8 < 2; ++e8) {
-            const int r0 = 32 * qb + 16 * e8 + 8 * hf;
-            const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[buf][r0]);
-            const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[buf][r0 + 4]);
-            const float4 d0 = *reinterpret_cast<const float4*>(&del_s[buf][r0]);
-            const float4 d1 = *reinterpret_cast<const float4*>(&del_s[buf][r0 + 4]);
-            const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-            const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            float p[8], ds[8];
-            if (diag) {
-              const int4 p0 = *reinterpret_cast<const int4*>(&qp_s[buf][r0]);
-              const int4 p1 = *reinterpret_cast<const int4*>(&qp_s[buf][r0 + 4]);
-              const int qv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                float x = fmaf(S[8 * e8 + i], c, -lv[i]);
-                if (ALIBI) x = fmaf(-sl2, (float)abs(qv[i] - my_kpos), x);
-                const bool vis = (q0 + r0 + i < Lq) && key_ok && (!causal || my_kpos <= qv[i]);
-                p[i] = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
-              }
-            } else {
-#pragma unroll
-              for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(S[8 * e8 + i], c, -lv[i]));
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ds[i] = p[i] * (dP[8 * e8 + i] - dv[i]);
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-              Pw[4 * e8 + i / 2] = ra_pack_bf16(p[i], p[i + 1]);
-              Dw[4 * e8 + i / 2] = ra_pack_bf16(ds[i], ds[i + 1]);
-            }
-          }
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const uint4 pa = make_uint4(Pw[4 * ks], Pw[4 * ks + 1], Pw[4 * ks + 2], Pw[4 * ks + 3]);
-            const uint4 da = make_uint4(Dw[4 * ks], Dw[4 * ks + 1], Dw[4 * ks + 2], Dw[4 * ks + 3]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              dV[dt] = ra_mfma32(pa, tile_col_frag(Os[buf], 32 * qb + 16 * ks, 32 * dt, lane), dV[dt]);
-              dK[dt] = ra_mfma32(da, tile_col_frag(Qs[buf], 32 * qb + 16 * ks, 32 * dt, lane), dK[dt]);
-            }
-          }
+        if (!diag) {
+          fast_item(buf);
+        } else {
+          masked_item(buf, q0, hq);
         }
       }
       if (!have_next) break;
