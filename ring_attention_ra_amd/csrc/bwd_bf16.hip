@@ -10,16 +10,19 @@
 //   dQ_i += scale * sum_j dS_ij k_j.
 // Two kernels, both deterministic (no atomics; every output element is owned
 // by one lane and accumulated in a fixed order):
-//  * bwd_dkdv_kernel: a work-group owns 128 keys (4 waves x 32) of one K/V
+//  * bwd_dkdv_kernel: a work-group owns 128 keys (4 blocks of 32) of one K/V
 //    head and walks every query head of its group and every 64-query tile that
-//    sees those keys. K and V fragments stay in registers. S = Q K^T and
-//    dP = dO V^T run with the query rows as the MFMA A operand (rows permuted
-//    so that each lane holds one key and 8 consecutive queries per k-step),
-//    which makes P^T and dS^T ready-made A operands for dV += P^T dO and
-//    dK += dS^T Q; dO and Q are read with the transposing LDS read. The
-//    accumulators need one wave per SIMD; on unmasked tiles the two 32-query
-//    halves of a tile are software-pipelined so that one half's exponentials
-//    run between the other half's matrix products.
+//    sees those keys. Each key block has two waves on one SIMD, split by
+//    output: the dV wave holds the K fragments and the dV accumulator and
+//    computes S = Q K^T, P and dV += P^T dO; the dK wave holds the V fragments
+//    and the dK accumulator and computes dP = dO V^T, reads P from LDS, and
+//    forms dS and dK += dS^T Q. Per tile: S | dP, then (barrier) dV | dS, dK;
+//    the two waves' matrix and vector work overlap on their SIMD, and the dK
+//    waves issue the next tile's copies in the slack of the first half. S and
+//    dP run with the query rows as the MFMA A operand (rows permuted so that
+//    each lane holds one key and 8 consecutive queries per k-step), which
+//    makes P^T and dS^T ready-made A operands of the next products; dO and Q
+//    are read with the transposing LDS read.
 //  * bwd_dq_kernel: a work-group owns 128 queries (4 waves x 32) and walks the
 //    key tiles, like the forward step: S^T = K Q^T and dP^T = V dO^T (Q and dO
 //    fragments in registers), then dQ^T += K^T dS^T with K^T from the
@@ -32,59 +35,67 @@
 namespace ra {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;       // dQ work-group: 4 waves x 32 queries
+constexpr int kThreadsKV = 512;     // dK/dV work-group: 4 key blocks x (dV wave, dK wave)
 constexpr int D = 128;
 constexpr int CPR = 16;             // 16-byte chunks per row
 constexpr int KK = D / 16;          // k-steps over d
 constexpr int DT = D / 32;          // 32-wide d tiles
 constexpr int TROWS = 64;           // rows per streamed tile
 constexpr int SLOTS = TROWS * CPR;  // 16-byte slots per tile
-constexpr int DMA_PER_WAVE = SLOTS / (4 * 64);
 
 __device__ __forceinline__ float safe_lse2(float lse) {
   // exp2(x - lse2) must give 0 for a row that saw no key (lse = -inf).
   return lse == -INFINITY ? INFINITY : lse * RA_LOG2E;
 }
 
-// Byte offsets (within a full tile) of this lane's DMA slots.
-__device__ __forceinline__ void dma_offsets(uint32_t (&off)[DMA_PER_WAVE], int wave, int lane) {
+// A 64-row tile is copied by NW waves, DPW = SLOTS / (64 * NW) 16-byte slots
+// per lane; slot p holds row p / 16, physical chunk p % 16 (tile_swz layout).
+template <int NW>
+struct TileCopy {
+  static constexpr int DPW = SLOTS / (64 * NW);
+  uint32_t off[DPW];  // byte offsets of this lane's slots within a full tile
+  __device__ __forceinline__ TileCopy(int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int p = (wave * DMA_PER_WAVE + i) * 64 + lane;
-    const int r = p / CPR, ph = p % CPR;
-    off[i] = (uint32_t)(r * D + 8 * (ph ^ tile_swz(r))) * 2;
-  }
-}
-
-// Copy rows [row0, row0 + 64) of a [L, 128] bf16 matrix into a swizzled LDS
-// tile; rows at or past L are clamped to L - 1 (the caller masks them).
-__device__ __forceinline__ void dma_tile(uint4* tile, const uint16_t* base, int row0, int L, int wave,
-                                         int lane, const uint32_t (&off)[DMA_PER_WAVE]) {
-  const char* t = reinterpret_cast<const char*>(base + (int64_t)row0 * D);
-  if (row0 + TROWS <= L) {
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) dma16(t + off[i], &tile[(wave * DMA_PER_WAVE + i) * 64]);
-  } else {
-    const int last = L - 1 - row0;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int bs = (wave * DMA_PER_WAVE + i) * 64, p = bs + lane, r = p / CPR, ph = p % CPR;
-      dma16(t + (uint32_t)(min(r, last) * D + 8 * (ph ^ tile_swz(r))) * 2, &tile[bs]);
+    for (int i = 0; i < DPW; ++i) {
+      const int p = (wave * DPW + i) * 64 + lane;
+      const int r = p / CPR, ph = p % CPR;
+      off[i] = (uint32_t)(r * D + 8 * (ph ^ tile_swz(r))) * 2;
     }
   }
-}
+  // Copy rows [row0, row0 + 64) of a [L, 128] bf16 matrix (0 <= row0 < L);
+  // rows at or past L are clamped to L - 1 (the caller masks them).
+  __device__ __forceinline__ void copy(uint4* tile, const uint16_t* base, int row0, int L, int wave,
+                                       int lane) const {
+    const char* t = reinterpret_cast<const char*>(base + (int64_t)row0 * D);
+    if (row0 + TROWS <= L) {
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) dma16(t + off[i], &tile[(wave * DPW + i) * 64]);
+    } else {
+      const int last = L - 1 - row0;
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int bs = (wave * DPW + i) * 64, p = bs + lane, r = p / CPR, ph = p % CPR;
+        dma16(t + (uint32_t)(min(r, last) * D + 8 * (ph ^ tile_swz(r))) * 2, &tile[bs]);
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
 
 template <bool ALIBI>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+__global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
   __shared__ uint4 Qs[2][SLOTS];
   __shared__ uint4 Os[2][SLOTS];  // dO
   __shared__ __align__(16) float lse_s[2][TROWS];
   __shared__ __align__(16) float del_s[2][TROWS];
   __shared__ __align__(16) int qp_s[2][TROWS];
+  // P of the current tile, handed from each key block's dV wave to its dK
+  // wave: [key block][query half][element quad][lane], 4 floats each.
+  __shared__ float4 Px[4][2][4][64];
 
   const int Lq = a.len_q, Lkv = a.len_kv;
   const int g = a.heads_q / a.heads_kv;
@@ -94,7 +105,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
 
   const int tid = threadIdx.x;
   const int wave = uniform_i(tid >> 6), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int k0 = kt * 128, kw0 = k0 + 32 * wave;
+  // Waves kb and kb + 4 share a SIMD and key block kb: the first computes
+  // S, P and dV, the second dP, dS and dK.
+  const int kb = wave & 3;
+  const bool dv_wave = wave < 4;
+  const int k0 = kt * 128, kw0 = k0 + 32 * kb;
   const int key = kw0 + l32;
   const bool key_ok = key < Lkv;
   const bool wave_active = kw0 < Lkv;
@@ -102,16 +117,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
   const float c = a.scale * RA_LOG2E;
 
   const int64_t khead = (int64_t)b * a.heads_kv + hk;
-  const auto rk = make_rsrc(static_cast<const uint16_t*>(a.k) + khead * Lkv * D, (int64_t)Lkv * D * 2);
-  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.v) + khead * Lkv * D, (int64_t)Lkv * D * 2);
-
-  // K and V fragments: B operands of S = Q K^T and dP = dO V^T (lane = key).
-  uint4 kf[KK], vf[KK];
+  // K fragments (B operand of S = Q K^T) for the dV wave, V fragments (B
+  // operand of dP = dO V^T) for the dK wave; lane = key.
+  const auto rkv = make_rsrc(static_cast<const uint16_t*>(dv_wave ? a.k : a.v) + khead * Lkv * D,
+                             (int64_t)Lkv * D * 2);
+  uint4 bf[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    kf[kk] = buf_load16(rk, (uint32_t)(key * D + 16 * kk + 8 * hf) * 2);
-    vf[kk] = buf_load16(rv, (uint32_t)(key * D + 16 * kk + 8 * hf) * 2);
-  }
+  for (int kk = 0; kk < KK; ++kk) bf[kk] = buf_load16(rkv, (uint32_t)(key * D + 16 * kk + 8 * hf) * 2);
   const int my_kpos = key_ok ? a.k_pos[key] : INT32_MAX;
   const int kmin_w = wave_active ? a.k_pos[kw0] : INT32_MAX;
   const int kmax_w = wave_active ? a.k_pos[min(kw0 + 31, Lkv - 1)] : INT32_MAX;
@@ -131,23 +143,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
   const int nq = (Lq + TROWS - 1) / TROWS - qt0;
   const int n_items = nq > 0 ? g * nq : 0;
 
-  ra_f32x16 dK[DT], dV[DT];
+  ra_f32x16 acc[DT];  // dV (dV wave) or dK / scale (dK wave)
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dK[dt] = ra_f32x16{};
-    dV[dt] = ra_f32x16{};
-  }
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = ra_f32x16{};
 
   if (n_items > 0) {
-    uint32_t off[DMA_PER_WAVE];
-    dma_offsets(off, wave, lane);
+    // The dK waves copy the tiles (in their slack at the end of the first
+    // phase of the previous item); the dV waves copy nothing.
+    const TileCopy<4> tc(kb, lane);
     auto item_head = [&](int it) { return hk * g + it / nq; };
     auto item_q0 = [&](int it) { return (qt0 + it % nq) * TROWS; };
     auto load_item = [&](int buf, int it) {
       const int hq = item_head(it), q0 = item_q0(it);
       const int64_t qhead = (int64_t)b * a.heads_q + hq;
-      dma_tile(Qs[buf], static_cast<const uint16_t*>(a.q) + qhead * Lq * D, q0, Lq, wave, lane, off);
-      dma_tile(Os[buf], static_cast<const uint16_t*>(a.d_o) + qhead * Lq * D, q0, Lq, wave, lane, off);
+      tc.copy(Qs[buf], static_cast<const uint16_t*>(a.q) + qhead * Lq * D, q0, Lq, kb, lane);
+      tc.copy(Os[buf], static_cast<const uint16_t*>(a.d_o) + qhead * Lq * D, q0, Lq, kb, lane);
     };
     struct RowVals { float lse, del; int qp; };
     auto load_rows = [&](int it) {
@@ -169,60 +179,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
       }
     };
 
-    // An item with masked elements (across the diagonal, ragged, or ALiBi):
-    // one 32-query block after the other, masked per element.
-    auto masked_item = [&](int buf, int q0, int hq) {
-      const float sl2 = ALIBI ? a.slopes[hq] * RA_LOG2E : 0.0f;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        ra_f32x16 S = ra_f32x16{}, dP = ra_f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          S = ra_mfma32(tile_row_frag(Qs[buf], 32 * qb, kk, lane), kf[kk], S);
-          dP = ra_mfma32(tile_row_frag(Os[buf], 32 * qb, kk, lane), vf[kk], dP);
-        }
-        // Lane element e: key `key`, query row 32*qb + 16*(e/8) + 8*hf + e%8.
-        uint32_t Pw[8], Dw[8];
-#pragma unroll
-        for (int e8 = 0; e8 < 2; ++e8) {
-          const int r0 = 32 * qb + 16 * e8 + 8 * hf;
-          const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[buf][r0]);
-          const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[buf][r0 + 4]);
-          const float4 d0 = *reinterpret_cast<const float4*>(&del_s[buf][r0]);
-          const float4 d1 = *reinterpret_cast<const float4*>(&del_s[buf][r0 + 4]);
-          const int4 p0 = *reinterpret_cast<const int4*>(&qp_s[buf][r0]);
-          const int4 p1 = *reinterpret_cast<const int4*>(&qp_s[buf][r0 + 4]);
-          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-          const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-          const int qv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-          float p[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            float x = fmaf(S[8 * e8 + i], c, -lv[i]);
-            if (ALIBI) x = fmaf(-sl2, (float)abs(qv[i] - my_kpos), x);
-            const bool vis = (q0 + r0 + i < Lq) && key_ok && (!causal || my_kpos <= qv[i]);
-            p[i] = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
-          }
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            Pw[4 * e8 + i / 2] = ra_pack_bf16(p[i], p[i + 1]);
-            Dw[4 * e8 + i / 2] =
-                ra_pack_bf16(p[i] * (dP[8 * e8 + i] - dv[i]), p[i + 1] * (dP[8 * e8 + i + 1] - dv[i + 1]));
-          }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const uint4 pa = make_uint4(Pw[4 * ks], Pw[4 * ks + 1], Pw[4 * ks + 2], Pw[4 * ks + 3]);
-          const uint4 da = make_uint4(Dw[4 * ks], Dw[4 * ks + 1], Dw[4 * ks + 2], Dw[4 * ks + 3]);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            dV[dt] = ra_mfma32(pa, tile_col_frag(Os[buf], 32 * qb + 16 * ks, 32 * dt, lane), dV[dt]);
-            dK[dt] = ra_mfma32(da, tile_col_frag(Qs[buf], 32 * qb + 16 * ks, 32 * dt, lane), dK[dt]);
-          }
-        }
-      }
-    };
-
     // Per-lane parts of the fragment addresses. A row fragment of rows
     // r0 + perm_row(lane%32), k-step kk sits at byte r0*256 + (kk/4)*128 +
     // rofs[kk%4]; a column fragment (tile_col_frag) of rows r0, columns 32*dt
@@ -231,14 +187,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     // add as constants).
     int rofs[4], cofs[2][2];
     {
-      const int pr = perm_row(l32), g = (lane >> 4) & 1, j = lane & 15;
+      const int pr = perm_row(l32), gq = (lane >> 4) & 1, j = lane & 15;
 #pragma unroll
       for (int m = 0; m < 4; ++m) rofs[m] = pr * 256 + ((2 * m + hf) ^ tile_swz(pr)) * 16;
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const int rl = 8 * hf + 4 * half + (j >> 2), x = 2 * g + ((j & 3) >> 1);
+          const int rl = 8 * hf + 4 * half + (j >> 2), x = 2 * gq + ((j & 3) >> 1);
           cofs[half][db] = rl * 256 + ((4 * db + x) ^ tile_swz(rl)) * 16 + 8 * (j & 1);
         }
     }
@@ -252,93 +208,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
       const uint2 a1 = lds_tr4(t + cofs[1][dt & 1]);
       return make_uint4(a0.x, a0.y, a1.x, a1.y);
     };
-    // An item every (query, key) pair of which is visible: no masks. With
-    // one wave per SIMD the overlap of matrix and vector work has to come
-    // from within the wave, so the code runs as
-    //   S, dP (block 0) | S, dP (block 1), P and dS of block 0 in between
-    //   | dV, dK (block 0), P and dS of block 1 in between | dV, dK (block 1)
-    // with a scheduling fence after every step, and fragments are read a few
-    // steps ahead of their products.
-    auto fast_item = [&](int buf) {
-      auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-      ra_f32x16 S[2], dP[2];
-      uint32_t Pw[2][8], Dw[2][8];
-      float lv[16], dv[16];  // lse, delta of the lane's 16 rows of one block
-      auto load_lsedel = [&](int qb) {
+    // One 32-query block's product A(rows) x bf^T: S (dV wave) or dP (dK wave).
+    constexpr int LA = 3;
+    auto row_product = [&](const uint4* tile, int qb) {
+      uint4 fr[LA + 1];
 #pragma unroll
-        for (int e8 = 0; e8 < 2; ++e8) {
-          const int r0 = 32 * qb + 16 * e8 + 8 * hf;
-          const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[buf][r0]);
-          const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[buf][r0 + 4]);
-          const float4 d0 = *reinterpret_cast<const float4*>(&del_s[buf][r0]);
-          const float4 d1 = *reinterpret_cast<const float4*>(&del_s[buf][r0 + 4]);
-          lv[8 * e8 + 0] = l0.x; lv[8 * e8 + 1] = l0.y; lv[8 * e8 + 2] = l0.z; lv[8 * e8 + 3] = l0.w;
-          lv[8 * e8 + 4] = l1.x; lv[8 * e8 + 5] = l1.y; lv[8 * e8 + 6] = l1.z; lv[8 * e8 + 7] = l1.w;
-          dv[8 * e8 + 0] = d0.x; dv[8 * e8 + 1] = d0.y; dv[8 * e8 + 2] = d0.z; dv[8 * e8 + 3] = d0.w;
-          dv[8 * e8 + 4] = d1.x; dv[8 * e8 + 5] = d1.y; dv[8 * e8 + 6] = d1.z; dv[8 * e8 + 7] = d1.w;
-        }
-      };
-      // VALU work of block qb for elements 2*j, 2*j + 1: P, dS, both packed.
-      auto valu = [&](int qb, int j) {
-        const int e = 2 * j;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[qb][e], c, -lv[e]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[qb][e + 1], c, -lv[e + 1]));
-        Pw[qb][j] = ra_pack_bf16(p0, p1);
-        Dw[qb][j] = ra_pack_bf16(p0 * (dP[qb][e] - dv[e]), p1 * (dP[qb][e + 1] - dv[e + 1]));
-      };
-      // S, dP of block qb; row fragments read LA k-steps ahead; extra(kk)
-      // runs between the k-steps.
-      constexpr int LA = 3;
-      auto sdp = [&](int qb, auto extra) {
-        uint4 qa[LA + 1], oa[LA + 1];
+      for (int kk = 0; kk < LA; ++kk) fr[kk] = row_frag(tile, 32 * qb, kk);
+      ra_f32x16 r = ra_f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < LA; ++kk) {
-          qa[kk] = row_frag(Qs[buf], 32 * qb, kk);
-          oa[kk] = row_frag(Os[buf], 32 * qb, kk);
-        }
-        S[qb] = ra_f32x16{};
-        dP[qb] = ra_f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          if (kk + LA < KK) {
-            qa[(kk + LA) % (LA + 1)] = row_frag(Qs[buf], 32 * qb, kk + LA);
-            oa[(kk + LA) % (LA + 1)] = row_frag(Os[buf], 32 * qb, kk + LA);
-          }
-          S[qb] = ra_mfma32(qa[kk % (LA + 1)], kf[kk], S[qb]);
-          dP[qb] = ra_mfma32(oa[kk % (LA + 1)], vf[kk], dP[qb]);
-          extra(kk);
-          fence();
-        }
-      };
-      // dV, dK of block qb; column fragments read one step ahead.
-      auto dvdk = [&](int qb, bool with_valu) {
-        uint4 ob[2], qbf[2];
-        ob[0] = col_frag(Os[buf], 32 * qb, 0);
-        qbf[0] = col_frag(Qs[buf], 32 * qb, 0);
-#pragma unroll
-        for (int st = 0; st < 2 * DT; ++st) {  // st = ks * DT + dt
-          const int ks = st / DT, dt = st % DT;
-          if (st + 1 < 2 * DT) {
-            const int ks1 = (st + 1) / DT, dt1 = (st + 1) % DT;
-            ob[(st + 1) & 1] = col_frag(Os[buf], 32 * qb + 16 * ks1, dt1);
-            qbf[(st + 1) & 1] = col_frag(Qs[buf], 32 * qb + 16 * ks1, dt1);
-          }
-          const uint4 pa = make_uint4(Pw[qb][4 * ks], Pw[qb][4 * ks + 1], Pw[qb][4 * ks + 2], Pw[qb][4 * ks + 3]);
-          const uint4 da = make_uint4(Dw[qb][4 * ks], Dw[qb][4 * ks + 1], Dw[qb][4 * ks + 2], Dw[qb][4 * ks + 3]);
-          dV[dt] = ra_mfma32(pa, ob[st & 1], dV[dt]);
-          dK[dt] = ra_mfma32(da, qbf[st & 1], dK[dt]);
-          if (with_valu) valu(1, st);
-          fence();
-        }
-      };
-      load_lsedel(0);
-      sdp(0, [](int) {});
-      sdp(1, [&](int kk) { valu(0, kk); });
-      load_lsedel(1);
-      dvdk(0, true);
-      dvdk(1, false);
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + LA < KK) fr[(kk + LA) % (LA + 1)] = row_frag(tile, 32 * qb, kk + LA);
+        r = ra_mfma32(fr[kk % (LA + 1)], bf[kk], r);
+      }
+      return r;
     };
-    load_item(0, 0);
+    // acc += W^T T for one 32-query block: W (8 packed bf16 pairs per lane)
+    // is P^T or dS^T, T the dO or Q tile read by column.
+    auto col_product = [&](const uint4* tile, int qb, const uint32_t (&W)[8]) {
+      uint4 cf[2];
+      cf[0] = col_frag(tile, 32 * qb, 0);
+#pragma unroll
+      for (int st = 0; st < 2 * DT; ++st) {  // st = ks * DT + dt
+        const int ks = st / DT, dt = st % DT;
+        if (st + 1 < 2 * DT) cf[(st + 1) & 1] = col_frag(tile, 32 * qb + 16 * ((st + 1) / DT), (st + 1) % DT);
+        const uint4 w = make_uint4(W[4 * ks], W[4 * ks + 1], W[4 * ks + 2], W[4 * ks + 3]);
+        acc[dt] = ra_mfma32(w, cf[st & 1], acc[dt]);
+      }
+    };
+
+    if (!dv_wave) load_item(0, 0);
     store_rows(0, load_rows(0));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -348,21 +246,87 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
       const int buf = it & 1;
       const bool have_next = it + 1 < n_items;
       RowVals nxt{0.f, 0.f, 0};
-      if (have_next) {
-        load_item(buf ^ 1, it + 1);
-        nxt = load_rows(it + 1);
-      }
+      if (have_next) nxt = load_rows(it + 1);
       const int hq = item_head(it), q0 = item_q0(it);
       // Positions of the item's first and last query row, from the LDS copy
       // (kept off the vector-memory counter that the tile copies use).
       const int qfirst = uniform_i(qp_s[buf][0]);
       const int qlast = uniform_i(qp_s[buf][TROWS - 1]);
-      if (wave_active && !(causal && qlast < kmin_w)) {
-        const bool diag = (q0 + TROWS > Lq) || (causal && qfirst < kmax_w) || ALIBI;
-        if (!diag) {
-          fast_item(buf);
+      const bool active = wave_active && !(causal && qlast < kmin_w);
+      const bool masked = (q0 + TROWS > Lq) || (causal && qfirst < kmax_w) || ALIBI;
+      // Lane element e of a block: key `key`, query row 32*qb + 16*(e/8) + 8*hf + e%8.
+      // Carried across the barrier in the same registers: dP = dO V^T of both
+      // blocks (dK wave), or P^T packed to bf16 pairs (dV wave, in hold[qb][0..7]).
+      ra_f32x16 hold[2];
+      uint32_t W[2][8];
+      if (active) {
+        if (dv_wave) {
+          const float sl2 = ALIBI ? a.slopes[hq] * RA_LOG2E : 0.0f;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const ra_f32x16 S = row_product(Qs[buf], qb);
+            float p[16];
+#pragma unroll
+            for (int e8 = 0; e8 < 2; ++e8) {
+              const int r0 = 32 * qb + 16 * e8 + 8 * hf;
+              const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[buf][r0]);
+              const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[buf][r0 + 4]);
+              const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+              if (masked) {
+                const int4 p0 = *reinterpret_cast<const int4*>(&qp_s[buf][r0]);
+                const int4 p1 = *reinterpret_cast<const int4*>(&qp_s[buf][r0 + 4]);
+                const int qv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                  float x = fmaf(S[8 * e8 + i], c, -lv[i]);
+                  if (ALIBI) x = fmaf(-sl2, (float)abs(qv[i] - my_kpos), x);
+                  const bool vis = (q0 + r0 + i < Lq) && key_ok && (!causal || my_kpos <= qv[i]);
+                  p[8 * e8 + i] = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
+                }
+              } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) p[8 * e8 + i] = __builtin_amdgcn_exp2f(fmaf(S[8 * e8 + i], c, -lv[i]));
+              }
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              Px[kb][qb][q4][lane] = make_float4(p[4 * q4], p[4 * q4 + 1], p[4 * q4 + 2], p[4 * q4 + 3]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) hold[qb][i] = __uint_as_float(ra_pack_bf16(p[2 * i], p[2 * i + 1]));
+          }
         } else {
-          masked_item(buf, q0, hq);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) hold[qb] = row_product(Os[buf], qb);
+        }
+      }
+      if (!dv_wave && have_next) load_item(buf ^ 1, it + 1);
+      __syncthreads();  // P of this tile is in Px
+      if (active) {
+        if (dv_wave) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) W[qb][i] = __float_as_uint(hold[qb][i]);
+            col_product(Os[buf], qb, W[qb]);
+          }
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+            for (int e8 = 0; e8 < 2; ++e8) {
+              const int r0 = 32 * qb + 16 * e8 + 8 * hf;
+              const float4 d0 = *reinterpret_cast<const float4*>(&del_s[buf][r0]);
+              const float4 d1 = *reinterpret_cast<const float4*>(&del_s[buf][r0 + 4]);
+              const float4 pa = Px[kb][qb][2 * e8][lane], pb = Px[kb][qb][2 * e8 + 1][lane];
+              const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+              const float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+              for (int i = 0; i < 8; i += 2)
+                W[qb][4 * e8 + i / 2] = ra_pack_bf16(p[i] * (hold[qb][8 * e8 + i] - dv[i]),
+                                                     p[i + 1] * (hold[qb][8 * e8 + i + 1] - dv[i + 1]));
+            }
+            col_product(Qs[buf], qb, W[qb]);
+          }
         }
       }
       if (!have_next) break;
@@ -372,11 +336,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
     }
   }
 
-  // Accumulate into dk_blk / dv_blk: element (dt, e) is key kw0 + 8*(e/4) +
-  // 4*hf + e%4, dim 32*dt + l32.
+  // Accumulate into dv_blk (dV wave) or dk_blk (dK wave): element (dt, e) is
+  // key kw0 + 8*(e/4) + 4*hf + e%4, dim 32*dt + l32.
   if (!wave_active) return;
-  float* dkh = a.dk + khead * Lkv * D;
-  float* dvh = a.dv + khead * Lkv * D;
+  float* outh = (dv_wave ? a.dv : a.dk) + khead * Lkv * D;
+  const float f = dv_wave ? 1.0f : a.scale;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -384,8 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a, int n_
       const int kr = kw0 + 8 * (e >> 2) + 4 * hf + (e & 3);
       if (kr < Lkv) {
         const int64_t idx = (int64_t)kr * D + 32 * dt + l32;
-        dkh[idx] += a.scale * dK[dt][e];
-        dvh[idx] += dV[dt][e];
+        outh[idx] += f * acc[dt][e];
       }
     }
   }
@@ -447,12 +410,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   for (int dt = 0; dt < DT; ++dt) dQ[dt] = ra_f32x16{};
   bool touched = false;
 
-  uint32_t off[DMA_PER_WAVE];
-  dma_offsets(off, wave, lane);
+  const TileCopy<4> tc(wave, lane);
   auto load_kp = [&](int kv0) { return tid < TROWS ? kpos[min(kv0 + tid, Lkv - 1)] : 0; };
 
-  dma_tile(Ks[0], kh, 0, Lkv, wave, lane, off);
-  dma_tile(Vs[0], vh, 0, Lkv, wave, lane, off);
+  tc.copy(Ks[0], kh, 0, Lkv, wave, lane);
+  tc.copy(Vs[0], vh, 0, Lkv, wave, lane);
   if (tid < TROWS) kp[0][tid] = load_kp(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -465,8 +427,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
     const bool have_next = kv0 + TROWS < Lkv;
     int kp_next = 0;
     if (have_next) {
-      dma_tile(Ks[buf ^ 1], kh, kv0 + TROWS, Lkv, wave, lane, off);
-      dma_tile(Vs[buf ^ 1], vh, kv0 + TROWS, Lkv, wave, lane, off);
+      tc.copy(Ks[buf ^ 1], kh, kv0 + TROWS, Lkv, wave, lane);
+      tc.copy(Vs[buf ^ 1], vh, kv0 + TROWS, Lkv, wave, lane);
       kp_next = load_kp(kv0 + TROWS);
     }
     const int kfirst = uniform_i(kp[buf][0]);
@@ -555,7 +517,8 @@ hipError_t launch_both(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dq_kernel<ALIBI>), dim3((unsigned)grid_q), dim3(kThreads), 0, stream, a, n_qtiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<ALIBI>), dim3((unsigned)grid_k), dim3(kThreads), 0, stream, a, n_ktiles);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<ALIBI>), dim3((unsigned)grid_k), dim3(kThreadsKV), 0, stream, a,
+                     n_ktiles);
   return hipGetLastError();
 }
 
