@@ -310,6 +310,8 @@ def _rel_err(got, ref):
     ("zigzag", True, True, 2, 1, 2, 320),          # ALiBi + GQA, ragged
     ("contiguous", False, False, 2, 2, 2, 200),    # no mask, ragged
     ("contiguous", True, True, 2, 2, 3, 128),
+    ("zigzag", True, False, 8, 2, 2, 64),          # 64-key chunk: two idle key blocks, one tile per head
+    ("contiguous", False, True, 4, 4, 1, 96),      # one rank, ALiBi without the causal mask
 ])
 def test_bwd_variants(layout, causal, alibi, hq, hkv, n, c):
     case = Case("bf16", 1, hq, hkv, 128, n * c, n, layout, causal, alibi, seed=61)
