@@ -259,6 +259,9 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
       // blocks (dK wave), or P^T packed to bf16 pairs (dV wave, in hold[qb][0..7]).
       ra_f32x16 hold[2];
       uint32_t W[2][8];
+      // The wave with vector work in a half has the longer path: it gets
+      // issue priority over its partner for that half.
+      if (dv_wave) __builtin_amdgcn_s_setprio(1);
       if (active) {
         if (dv_wave) {
           const float sl2 = ALIBI ? a.slopes[hq] * RA_LOG2E : 0.0f;
@@ -300,7 +303,9 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
         }
       }
       if (!dv_wave && have_next) load_item(buf ^ 1, it + 1);
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();  // P of this tile is in Px
+      if (!dv_wave) __builtin_amdgcn_s_setprio(1);
       if (active) {
         if (dv_wave) {
 #pragma unroll
@@ -329,6 +334,7 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (!have_next) break;
       store_rows(buf ^ 1, nxt);
       __builtin_amdgcn_s_waitcnt(0);
