@@ -13,8 +13,8 @@ Pages are cited by host and section:
 * discosf.com  -- practitioner article on context parallelism and Ring
   Attention (article heading "百万Token上下文训练的挑战与突破").
 * digipub.cc   -- "大模型如何訓練百萬 Token 上下文：上下文并行與 Ring Attention".
-* intelliparadigm.com -- long-context survey (positional encodings,
-  FlashAttention).
+* intelliparadigm.com -- long-context survey (positional encodings, including
+  RoPE in ``rope_fp64``, and FlashAttention).
 
 Parity status: every public function here is pinned by ``tests/test_oracle.py``
 (brute force, closed forms, torch fp64 SDPA / autograd, finite differences and
@@ -36,3 +36,4 @@ from .attention_fp64 import (  # noqa: F401
     ring_schedule,
     visible_pairs,
 )
+from .rope_fp64 import inv_freq, rotary_embedding  # noqa: F401
