@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 import seeded_inputs as si  # noqa: E402
 from ring_attention_ra_amd import _lib, configs, ring  # noqa: E402
 
+PEAK_HBM_TBS = 8.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
@@ -221,6 +222,26 @@ def main():
         "visible_pairs_per_head": sum(pairs),
         "fwd_flop_per_step": fwd_flops,
     }
+    # Rotary position embedding of the rank's K chunks (every chunk by its own
+    # global positions), out of place, as a separate HBM-bound pass: not part
+    # of the step above, timed after it with HIP events on the same stream.
+    k_rot = torch.empty_like(k_ch)
+    rope_ev = []
+    for it in range(4):
+        if it == 1:
+            rope_ev.append(torch.cuda.Event(enable_timing=True))
+            rope_ev[-1].record()
+        for s_ in range(n):
+            _lib.ra_rope(k_ch[s_], k_rot[s_], pos[s_])
+    rope_ev.append(torch.cuda.Event(enable_timing=True))
+    rope_ev[-1].record()
+    torch.cuda.synchronize()
+    rope_ms = rope_ev[0].elapsed_time(rope_ev[1]) / 3
+    rope_bytes = 2.0 * k_ch.numel() * k_ch.element_size() + pos.numel() * 4
+    del k_rot
+    extra["rope"] = {"kernel": "rope_kernel (ra_rope)", "tensor": "K chunks [N,B,Hkv,C,D]", "ms": round(rope_ms, 4),
+                     "gbs": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm": round(rope_bytes / (rope_ms * 1e-3) / 1e12 / PEAK_HBM_TBS, 4)}
     if w.backward:
         bwd_ms = pair_ms(bwd_events)
         bwd_total_ms = sum(bwd_ms) / args.steps

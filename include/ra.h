@@ -93,6 +93,22 @@ ra_status ra_layout_permute(const void* src, void* dst, int32_t* pos, int64_t ou
                             int64_t seq_len, int32_t row_elems, int32_t dtype, int32_t n_ranks,
                             int32_t layout, int32_t rank, int32_t inverse, void* stream);
 
+/* Rotary position embedding (intelliparadigm.com long-context survey, §2.1.3
+ * RoPE的旋转位置编码), applied to `outer` independent slabs of len rows of
+ * head_dim elements: x and y are [outer, len, head_dim] in `dtype`. In each
+ * row, element j of the first half pairs with element j of the second half
+ * (d = head_dim, a = pos[t] * base^(-2j/d)):
+ *   y[j] = x[j] cos a - x[j + d/2] sin a,   y[j + d/2] = x[j] sin a + x[j + d/2] cos a.
+ * pos: int32 [len], the GLOBAL positions of the rows (non-negative), e.g. the
+ * output of ra_positions for a rank's chunk, so either layout gets the rotation
+ * its tokens have in the whole sequence; it is shared by all slabs.
+ * The angle is reduced exactly (in double precision) and the rotation done in
+ * fp32; bf16 results round to nearest even. y may be x (in place) but may not
+ * overlap it otherwise. Errors: head_dim odd or outside [2, 256], base not
+ * positive and finite, NULL pointers when there is work, unknown dtype. */
+ra_status ra_rope(const void* x, void* y, const int32_t* pos, int64_t outer, int64_t len,
+                  int32_t head_dim, int32_t dtype, float base, void* stream);
+
 /* Start state of the running accumulators: o_acc = 0 [B,Hq,Lq,D], m = -inf and
  * l = 0 [B,Hq,Lq] (the initial max and sum of the online softmax,
  * intelliparadigm.com §3.1.2). All fp32. Only batch, heads_q, head_dim and

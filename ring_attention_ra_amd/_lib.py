@@ -50,6 +50,7 @@ _DIMS = ctypes.POINTER(RaDims)
 _SIGNATURES = {
     "ra_positions": [_I64, _I32, _I32, _I32, _P, _P],
     "ra_layout_permute": [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P],
+    "ra_rope": [_P, _P, _P, _I64, _I64, _I32, _I32, _F32, _P],
     "ra_state_init": [_DIMS, _P, _P, _P, _P],
     "ra_step_fwd": [_DIMS, _P, _P, _P, _P, _P, _I32, _F32, _P, _P, _P, _P, _P],
     "ra_finalize": [_DIMS, _P, _P, _P, _P, _P, _P],
@@ -152,6 +153,18 @@ def ra_layout_permute(src, dst, pos, outer, seq_len, row_elems, n_ranks, layout,
                                    _ptr(pos, "pos", torch.int32, allow_none=True), outer, seq_len,
                                    row_elems, dtype_code(src.dtype), n_ranks, lay, rank, int(inverse),
                                    _stream(stream)), "ra_layout_permute")
+
+
+def ra_rope(x, y, pos, base=10000.0, stream=None):
+    """RoPE of x ``[..., L, D]`` into y (may be x) at the int32 positions ``[L]``."""
+    if x.dtype != y.dtype or x.shape != y.shape:
+        raise ValueError("x and y must have the same dtype and shape")
+    if x.dim() < 2:
+        raise ValueError("x must be [..., L, D]")
+    length, d = x.shape[-2], x.shape[-1]
+    outer = x.numel() // max(length * d, 1)
+    _check(lib().ra_rope(_ptr(x, "x"), _ptr(y, "y"), _ptr(pos, "pos", torch.int32, length), outer, length, d,
+                         dtype_code(x.dtype), float(base), _stream(stream)), "ra_rope")
 
 
 def ra_state_init(dims, o_acc, m, l, stream=None):

@@ -116,6 +116,25 @@ ra_status ra_layout_permute(const void* src, void* dst, int32_t* pos, int64_t ou
   return launch_result(launch_permute(a, (hipStream_t)stream), "ra_layout_permute");
 }
 
+ra_status ra_rope(const void* x, void* y, const int32_t* pos, int64_t outer, int64_t len,
+                  int32_t head_dim, int32_t dtype, float base, void* stream) {
+  if (outer < 0 || len < 0) return fail(RA_ERR_INVALID_ARGUMENT, "negative outer or len");
+  if (!dtype_ok(dtype)) return fail(RA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (head_dim < 2 || head_dim > 256 || head_dim % 2)
+    return fail(RA_ERR_INVALID_ARGUMENT, "head_dim must be even and in [2, 256] (got %d)", head_dim);
+  if (!(base > 0.0f) || !std::isfinite(base))
+    return fail(RA_ERR_INVALID_ARGUMENT, "base must be positive and finite");
+  if (outer == 0 || len == 0) return RA_OK;
+  if (!x || !y || !pos) return fail(RA_ERR_INVALID_ARGUMENT, "x, y or pos is NULL");
+  const int64_t bytes = outer * len * head_dim * dtype_size(dtype);
+  const char* xs = (const char*)x;
+  const char* ys = (const char*)y;
+  if (xs != ys && xs < ys + bytes && ys < xs + bytes)
+    return fail(RA_ERR_INVALID_ARGUMENT, "x and y overlap without being the same tensor");
+  return launch_result(launch_rope(x, y, pos, outer, len, head_dim, dtype, base, (hipStream_t)stream),
+                       "ra_rope");
+}
+
 ra_status ra_state_init(const ra_dims* d, float* o_acc, float* m, float* l, void* stream) {
   bool empty = false;
   ra_status st = check_dims(d, &empty);

@@ -79,6 +79,8 @@ hipError_t launch_finalize(const float* o_acc, const float* m, const float* l, v
 hipError_t launch_bwd_delta(const void* o, const void* d_o, float* delta, int64_t rows,
                             int32_t head_dim, int32_t dtype, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t outer, int64_t len, int32_t d,
+                       int32_t dtype, float base, hipStream_t stream);
 
 }  // namespace ra
 

@@ -89,6 +89,29 @@ def test_permute_validation():
     assert L.ra_layout_permute(None, base, None, 1, 16, 8, 0, 4, 0, -1, 0, None) == 1
 
 
+def test_rope_validation():
+    buf = ctypes.create_string_buffer(4096)
+    base = ctypes.addressof(buf)
+    ok = (base, base, base + 2048, 2, 4, 64, 0, 10000.0, None)
+    bad = [
+        ((base, base, base + 2048, 2, 4, 63, 0, 10000.0, None), "even"),      # odd head_dim
+        ((base, base, base + 2048, 2, 4, 258, 0, 10000.0, None), "even"),     # too wide
+        ((base, base, base + 2048, 2, 4, 64, 7, 10000.0, None), "dtype"),
+        ((base, base, base + 2048, 2, 4, 64, 0, 0.0, None), "base"),
+        ((base, base, base + 2048, 2, 4, 64, 0, float("inf"), None), "base"),
+        ((base, base, None, 2, 4, 64, 0, 10000.0, None), "NULL"),
+        ((base, base + 2, base + 2048, 2, 4, 64, 0, 10000.0, None), "overlap"),
+        ((base, base, base + 2048, -1, 4, 64, 0, 10000.0, None), "negative"),
+    ]
+    for args, needle in bad:
+        assert L.ra_rope(*args) == 1
+        assert needle in _lib.ra_last_error()
+    # no work: nothing is validated beyond the shape and nothing is launched
+    assert L.ra_rope(None, None, None, 0, 4, 64, 0, 10000.0, None) == 0
+    assert L.ra_rope(None, None, None, 2, 0, 64, 0, 10000.0, None) == 0
+    assert ok  # the valid form launches, which needs a GPU: covered by the GPU tests
+
+
 def test_bwd_validation():
     d = _dims(dt=_lib.RA_FP32, d=64)
     args = [ctypes.byref(d)] + [1] * 5 + [1, 0.1, None] + [1] * 6 + [None]
