@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=str(configs.HEADLINE.index),
-                    help="workload index (1-5) or name; default: the 128K zig-zag share")
+                    help="workload index (1-6) or name; default: the 128K zig-zag share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows in the CPU-baseline sample")
     ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-baseline sample")

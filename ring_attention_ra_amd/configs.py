@@ -1,4 +1,4 @@
-"""The five workloads of the ring-attention step, by name and shape.
+"""The workloads of the ring-attention step, by name and shape.
 
 Each is one rank's share of a causal ring: a query chunk of C = S / N tokens
 attending to the N K/V chunks it receives around the ring. Inputs are
@@ -53,6 +53,10 @@ WORKLOADS = [
              "contiguous", 3, alibi=True, std=math.sqrt(0.5)),
     Workload(5, "bf16-h16-d128-s1m-n64-zigzag-r63-fwdbwd", "bf16", 1, 16, 16, 128, 1048576, 64,
              "zigzag", 63, backward=True),
+    # The GQA + ALiBi contiguous share with its backward step (the backward on
+    # the contiguous / GQA / ALiBi configuration).
+    Workload(6, "bf16-gqa64x8-d128-s64k-n4-contiguous-r3-alibi-fwdbwd", "bf16", 1, 64, 8, 128, 65536, 4,
+             "contiguous", 3, alibi=True, std=math.sqrt(0.5), backward=True),
 ]
 
 BY_NAME = {w.name: w for w in WORKLOADS}

@@ -139,9 +139,13 @@ def test_ring_schedule_and_slopes_agree_with_oracle():
 
 
 def test_workloads_match_their_names():
-    assert len(configs.WORKLOADS) == 5
+    assert len(configs.WORKLOADS) == 6
+    assert [w.index for w in configs.WORKLOADS] == list(range(1, 7))
     for w in configs.WORKLOADS:
         assert w.seq_len % w.n_ranks == 0 and 0 <= w.rank < w.n_ranks
         assert w.heads_q % w.heads_kv == 0
     assert configs.HEADLINE.seq_len == 131072 and configs.HEADLINE.layout == "zigzag"
     assert math.isclose(configs.get(4).std ** 2, 0.5)
+    w4, w6 = configs.get(4), configs.get(6)
+    assert (w6.heads_q, w6.heads_kv, w6.seq_len, w6.layout, w6.alibi, w6.backward) == \
+        (w4.heads_q, w4.heads_kv, w4.seq_len, w4.layout, True, True)

@@ -337,6 +337,46 @@ def test_bwd_deterministic():
     assert a == b
 
 
+def test_workload_gqa_alibi_contiguous_backward_sampled():
+    """Full-size forward + backward of the 64K GQA 64/8 + ALiBi contiguous share
+    (rank 3); the oracle recomputes, for one key/value head and its eight query
+    heads, dQ on sampled rows and dK, dV on sampled keys near the end of the
+    sequence (seen by few rows under the causal mask)."""
+    w = configs.get(6)
+    case = Case(w.dtype, w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seq_len, w.n_ranks, w.layout,
+                w.causal, w.alibi, w.std, seed=w.index)
+    log(f"case {w.name} (backward, sampled)")
+    with Timer("draw + GPU forward/backward"):
+        q, k, v, do = draw(case, with_do=True)
+        dq, dk, dv = _bwd_gpu(case, w.rank, q, k, v, do)
+    g = w.heads_q // w.heads_kv
+    kv_heads = [5]
+    qheads = [hk * g + i for hk in kv_heads for i in range(g)]
+    c, n, s = w.chunk, w.n_ranks, w.seq_len
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([np.arange(6), np.arange(c - 6, c), rng.integers(0, c, 12)]))
+    keys = np.unique(np.concatenate([np.arange(s - 16, s), rng.integers(s - 96, s, 6)]))
+    with Timer("host copies"):
+        qh, kh, vh = host_heads(q, qheads), host_heads(k, kv_heads), host_heads(v, kv_heads)
+        doh = do.float().cpu().numpy()
+    with Timer("oracle"):
+        dq_r, dk_r, dv_r = oracle.attention_rank_share_bwd(qh, kh, vh, doh, n, w.rank, w.layout, w.causal,
+                                                           w.scale, oracle_slopes(case), rows=rows, keys=keys,
+                                                           kv_heads=kv_heads)
+    owner = oracle.owner_rank(keys, s, n, w.layout)
+    local = keys // n if w.layout == "zigzag" else keys % c
+    hsel = torch.tensor(kv_heads, device=dk.device)
+    dk_g = np.stack([host64(dk[int(owner[i])].index_select(1, hsel)[:, :, int(local[i])])
+                     for i in range(keys.size)], axis=2)
+    dv_g = np.stack([host64(dv[int(owner[i])].index_select(1, hsel)[:, :, int(local[i])])
+                     for i in range(keys.size)], axis=2)
+    dq_g = host64(dq[:, qheads][:, :, rows])
+    e_q, e_k, e_v = _rel_err(dq_g, dq_r), _rel_err(dk_g, dk_r), _rel_err(dv_g, dv_r)
+    log(f"  rows={rows.size} keys={keys.size}: rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g}")
+    assert e_q <= BWD_REL and e_k <= BWD_REL and e_v <= BWD_REL
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
 def test_workload_1m_zigzag_backward_sampled():
     """Full-size forward + backward of the 1M-token zig-zag share; the oracle
     recomputes dQ on sampled rows and dK, dV on sampled late keys (few rows see
