@@ -3,7 +3,7 @@
 A step is one pass of the whole path for the rank under study: the layout
 permutation of its query chunk and of every K/V chunk out of global order
 (ra_layout_permute), the accumulator start state, one ra_step_fwd per chunk
-in ring order, ra_finalize, and -- for the workload that has one -- the
+in ring order, ra_finalize, and -- for the workloads that have one -- the
 backward ring (ra_bwd_delta + one ra_step_bwd per chunk). Inputs are seeded
 synthetic tensors already resident in HBM when the timed region starts.
 
@@ -12,6 +12,9 @@ Prints one JSON line. `value` is causal-effective TFLOP/s of the whole step
 10*D). `roofline` is the dominant kernel (the bf16 step kernel) timed live
 with HIP events on the stream it runs on. `cpu_baseline` is the fp64 oracle
 timed on a bounded sample of the same workload on the host cores.
+`breakdown` adds the layout permutation's rate, the backward at 8*D per pair
+(without the recomputed S) next to the 10*D figure, and the rotary position
+embedding of the rank's K chunks, timed after the step as a separate pass.
 """
 
 from __future__ import annotations
@@ -247,6 +250,8 @@ def main():
         bwd_total_ms = sum(bwd_ms) / args.steps
         extra["bwd_kernel_ms_per_step"] = round(bwd_total_ms, 4)
         extra["bwd_kernel_tflops"] = round(bwd_flops / (bwd_total_ms * 1e-3) / 1e12, 2)
+        # The same time counted without the recomputed S (8*D per visible pair).
+        extra["bwd_kernel_tflops_8d"] = round(0.8 * bwd_flops / (bwd_total_ms * 1e-3) / 1e12, 2)
         extra["bwd_flop_per_step"] = bwd_flops
 
     result = {
