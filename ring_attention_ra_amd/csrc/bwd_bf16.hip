@@ -30,6 +30,8 @@
 // Tiles stream through double-buffered LDS via the DMA path; fully masked
 // tiles are skipped from the positions (which increase), and only tiles
 // across the diagonal (or ragged, or with ALiBi) are masked per element.
+#include <type_traits>
+
 #include "tile_common.h"
 
 namespace ra {
@@ -265,38 +267,46 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
       if (active) {
         if (dv_wave) {
           const float sl2 = ALIBI ? a.slopes[hq] * RA_LOG2E : 0.0f;
+          // The mask test is hoisted out of the block loop, so each variant is
+          // one straight-line stretch in which the second block's products can
+          // issue among the first block's exponentials.
+          auto s_and_p = [&](auto masked_tag) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const ra_f32x16 S = row_product(Qs[buf], qb);
-            float p[16];
+            for (int qb = 0; qb < 2; ++qb) {
+              const ra_f32x16 S = row_product(Qs[buf], qb);
+              float p[16];
 #pragma unroll
-            for (int e8 = 0; e8 < 2; ++e8) {
-              const int r0 = 32 * qb + 16 * e8 + 8 * hf;
-              const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[buf][r0]);
-              const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[buf][r0 + 4]);
-              const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-              if (masked) {
-                const int4 p0 = *reinterpret_cast<const int4*>(&qp_s[buf][r0]);
-                const int4 p1 = *reinterpret_cast<const int4*>(&qp_s[buf][r0 + 4]);
-                const int qv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+              for (int e8 = 0; e8 < 2; ++e8) {
+                const int r0 = 32 * qb + 16 * e8 + 8 * hf;
+                const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[buf][r0]);
+                const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[buf][r0 + 4]);
+                const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                if constexpr (MASKED) {
+                  const int4 p0 = *reinterpret_cast<const int4*>(&qp_s[buf][r0]);
+                  const int4 p1 = *reinterpret_cast<const int4*>(&qp_s[buf][r0 + 4]);
+                  const int qv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                  float x = fmaf(S[8 * e8 + i], c, -lv[i]);
-                  if (ALIBI) x = fmaf(-sl2, (float)abs(qv[i] - my_kpos), x);
-                  const bool vis = (q0 + r0 + i < Lq) && key_ok && (!causal || my_kpos <= qv[i]);
-                  p[8 * e8 + i] = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
+                  for (int i = 0; i < 8; ++i) {
+                    float x = fmaf(S[8 * e8 + i], c, -lv[i]);
+                    if (ALIBI) x = fmaf(-sl2, (float)abs(qv[i] - my_kpos), x);
+                    const bool vis = (q0 + r0 + i < Lq) && key_ok && (!causal || my_kpos <= qv[i]);
+                    p[8 * e8 + i] = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
+                  }
+                } else {
+#pragma unroll
+                  for (int i = 0; i < 8; ++i) p[8 * e8 + i] = __builtin_amdgcn_exp2f(fmaf(S[8 * e8 + i], c, -lv[i]));
                 }
-              } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) p[8 * e8 + i] = __builtin_amdgcn_exp2f(fmaf(S[8 * e8 + i], c, -lv[i]));
               }
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4)
+                Px[kb][qb][q4][lane] = make_float4(p[4 * q4], p[4 * q4 + 1], p[4 * q4 + 2], p[4 * q4 + 3]);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) hold[qb][i] = __uint_as_float(ra_pack_bf16(p[2 * i], p[2 * i + 1]));
             }
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-              Px[kb][qb][q4][lane] = make_float4(p[4 * q4], p[4 * q4 + 1], p[4 * q4 + 2], p[4 * q4 + 3]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) hold[qb][i] = __uint_as_float(ra_pack_bf16(p[2 * i], p[2 * i + 1]));
-          }
+          };
+          if (masked) s_and_p(std::true_type{});
+          else s_and_p(std::false_type{});
         } else {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) hold[qb] = row_product(Os[buf], qb);
