@@ -147,9 +147,12 @@ hipError_t launch_rope_t(const void* x, void* y, const int32_t* pos, int64_t row
                          double log2_base, hipStream_t stream) {
   const int groups = (d >> 1) / VEC;
   const int threads = 256;
-  int64_t blocks = (rows * groups + threads - 1) / threads;
-  blocks = std::max<int64_t>(1, std::min<int64_t>(blocks, 256 * 64));
   const int fixed = threads % groups == 0 ? 1 : 0;
+  // Four rows per thread where the groups fit a block evenly: the kernel's
+  // batched trip then runs, and each thread's angle setup serves four rows.
+  const int64_t per_thread = fixed ? 4 : 1;
+  int64_t blocks = (rows * groups + threads * per_thread - 1) / (threads * per_thread);
+  blocks = std::max<int64_t>(1, std::min<int64_t>(blocks, 256 * 64));
   hipLaunchKernelGGL((rope_kernel<T, VEC>), dim3((unsigned)blocks), dim3(threads), 0, stream,
                      static_cast<const T*>(x), static_cast<T*>(y), pos, rows, len, d, log2_base, fixed);
   return hipGetLastError();
