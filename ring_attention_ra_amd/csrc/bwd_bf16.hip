@@ -101,8 +101,12 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
 
   const int Lq = a.len_q, Lkv = a.len_kv;
   const int g = a.heads_q / a.heads_kv;
-  const int bh = blockIdx.x / n_ktiles;  // (batch, kv head)
-  const int kt = blockIdx.x - bh * n_ktiles;
+  // Key tiles in order of decreasing work across all heads (tile 0 sees the
+  // most queries under the causal mask), so the lightest work-groups come
+  // last; head bh then always lands on XCD bh % 8.
+  const int n_bh = (int)(gridDim.x / (unsigned)n_ktiles);
+  const int kt = blockIdx.x / n_bh;
+  const int bh = blockIdx.x - kt * n_bh;  // (batch, kv head)
   const int b = bh / a.heads_kv, hk = bh - b * a.heads_kv;
 
   const int tid = threadIdx.x;
@@ -381,8 +385,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   __shared__ __align__(16) int kp[2][TROWS];
 
   const int Lq = a.len_q, Lkv = a.len_kv;
-  const int bh = blockIdx.x / n_qtiles;
-  const int qt = n_qtiles - 1 - (blockIdx.x - bh * n_qtiles);  // heaviest first under causal
+  // Query tiles in order of decreasing work across all heads (the last tile
+  // sees the most keys under the causal mask); head bh lands on XCD bh % 8.
+  const int n_bh = (int)(gridDim.x / (unsigned)n_qtiles);
+  const int w = blockIdx.x / n_bh;
+  const int bh = blockIdx.x - w * n_bh;
+  const int qt = n_qtiles - 1 - w;
   const int b = bh / a.heads_q, h = bh - b * a.heads_q;
   const int hk = h / (a.heads_q / a.heads_kv);
 
