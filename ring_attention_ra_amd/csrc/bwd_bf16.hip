@@ -321,13 +321,15 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
       __syncthreads();  // P of this tile is in Px
       if (!dv_wave) __builtin_amdgcn_s_setprio(1);
       if (active) {
+        // W is P^T (dV wave) or dS^T (dK wave); both waves then run the same
+        // products from one call site, so the accumulator keeps one set of
+        // registers (two call sites made the compiler copy it out and back
+        // on every tile).
         if (dv_wave) {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
+          for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int i = 0; i < 8; ++i) W[qb][i] = __float_as_uint(hold[qb][i]);
-            col_product(Os[buf], qb, W[qb]);
-          }
         } else {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
@@ -344,9 +346,11 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
                 W[qb][4 * e8 + i / 2] = ra_pack_bf16(p[i] * (hold[qb][8 * e8 + i] - dv[i]),
                                                      p[i + 1] * (hold[qb][8 * e8 + i + 1] - dv[i + 1]));
             }
-            col_product(Qs[buf], qb, W[qb]);
           }
         }
+        const uint4* T = dv_wave ? Os[buf] : Qs[buf];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) col_product(T, qb, W[qb]);
       }
       __builtin_amdgcn_s_setprio(0);
       if (!have_next) break;
