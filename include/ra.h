@@ -122,10 +122,13 @@ ra_status ra_state_init(const ra_dims* d, float* o_acc, float* m, float* l, void
  * ALiBi term only when alibi_slopes != NULL, alibi_slopes being fp32 [Hq]);
  * with causal != 0 a key is visible only if k_pos[j] <= q_pos[i].
  * The state, all fp32 and updated in place, is defined over the keys J folded
- * in so far: m = max_J s, l = sum_J exp(s - m), o_acc = sum_J exp(s - m) v_j
- * (natural exponent). Rows with no visible key keep m = -inf, l = 0,
- * o_acc = 0. Chunks may be folded in any order; the result differs only by
- * rounding.
+ * in so far: m is the reference of the exponentials, l = sum_J exp(s - m) and
+ * o_acc = sum_J exp(s - m) v_j (natural exponent), so that m + ln l is the
+ * log-sum-exp of the row and o_acc / l its output whatever m is. The fp32
+ * path keeps m = max_J s; the bf16 path moves m only when the scores outgrow
+ * it, so that max_J s - 14 ln 2 <= m <= max_J s (and l >= 1). Rows with no
+ * visible key keep m = -inf, l = 0, o_acc = 0. Chunks may be folded in any
+ * order; the result differs only by rounding.
  * q_pos [Lq] and k_pos [Lkv] must be strictly increasing (both layouts give
  * that); tiles that are masked out entirely are skipped using this.
  * Positions must be non-negative. For bf16, q, k_blk, v_blk and o_acc must be

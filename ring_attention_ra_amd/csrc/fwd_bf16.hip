@@ -47,13 +47,15 @@
 //    follow one at a time with all waves in step, double-buffered, with
 //    per-element masks where needed.
 //  * The output is rescaled lazily: exponents are taken against a reference
-//    max that is raised (and O, l rescaled) only when a score exceeds it by
-//    more than 2^8; P then stays below 2^8, well inside bf16 / fp32 range.
-//    Over the fully visible tiles the multiply of O is skipped when no lane of
-//    the wave moved its reference (the common case after the first tiles). The
-//    true running max is tracked alongside, and the state is renormalised to
-//    it once before it is written, so memory holds exactly m = max s,
-//    l = sum exp(s - m), o_acc = sum exp(s - m) v.
+//    that is raised to the tile max (and O, l rescaled) only when the scores
+//    outgrow it. Over the fully visible tiles no row max is taken at all: the
+//    exponentials are computed against the reference first, and only when a
+//    lane's sum of P exceeds 2^14 (or the reference is still -inf) does the
+//    wave take the max, move the reference and redo them, so P stays below
+//    2^14, well inside bf16 / fp32 range. The masked tiles move it when the
+//    tile max exceeds it by more than 2^8. The reference is what is stored as
+//    m: l = sum exp(s - m) and o_acc = sum exp(s - m) v are taken against it,
+//    so m + ln l is the log-sum-exp, and max s - 14 ln 2 <= m <= max s.
 //  * Scores are kept in base-2 units (scale * log2 e folded into one FMA) and
 //    exponentiated with v_exp_f32; state in memory is in natural units.
 //  * Key tiles past the last query of the work-group are never visited
@@ -77,6 +79,7 @@ constexpr int BN = 64;   // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
+constexpr float kLimit = 16384.0f;  // bound on a lane's per-tile sum of P (> 32 * 2^kTau)
 
 enum TileMode { kFast = 0, kAlibiLinear = 1, kExact = 2 };
 
@@ -109,6 +112,39 @@ template <int NQK, int NPV>
 __device__ __forceinline__ void interleave_qk_first() {
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of QK products 0..3
   interleave_qk_step<NQK, NPV, 0>();
+}
+
+// Tile counts of a key chunk with increasing positions kpos:
+//   ra = #{u < na : kpos[u*BN] <= ba}         (first key of tile u)
+//   rb = #{u < nb : kpos[u*BN + BN - 1] <= bb} (last key of complete tile u)
+// Both by a 64-way search run together: each round every lane probes one
+// evenly spaced tile of each remaining range, and the ballot of the
+// (monotone) answers narrows each range to less than its probe spacing, so
+// a range of n tiles takes about log64(n) rounds of one load per lane.
+__device__ __forceinline__ void tile_counts(const int* kpos, int na, int ba, int nb, int bb, int lane,
+                                            int& ra, int& rb) {
+  int alo = 0, ahi = na, blo = 0, bhi = nb;
+  while (alo < ahi || blo < bhi) {
+    const int as = (ahi - alo + 63) >> 6, bs = (bhi - blo + 63) >> 6;
+    const int ap = alo + lane * as, bp = blo + lane * bs;
+    const bool aok = ap < ahi, bok = bp < bhi;
+    const int ak = aok ? kpos[ap * BN] : 0;
+    const int bk = bok ? kpos[bp * BN + BN - 1] : 0;
+    const int ac = __builtin_popcountll(__builtin_amdgcn_ballot_w64(aok && ak <= ba));
+    const int bc = __builtin_popcountll(__builtin_amdgcn_ballot_w64(bok && bk <= bb));
+    if (alo < ahi) {
+      const int lo = ac > 0 ? alo + (ac - 1) * as + 1 : alo;
+      ahi = min(ahi, alo + ac * as);
+      alo = lo;
+    }
+    if (blo < bhi) {
+      const int lo = bc > 0 ? blo + (bc - 1) * bs + 1 : blo;
+      bhi = min(bhi, blo + bc * bs);
+      blo = lo;
+    }
+  }
+  ra = alo;
+  rb = blo;
 }
 
 template <int D, bool ALIBI>
@@ -157,18 +193,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   const int* kpos = a.k_pos;
   const bool causal = a.causal != 0;
 
-  // Tiles the work-group visits: keys up to its last query (positions increase).
+  // Keys past the work-group's last query are never visible (positions
+  // increase): when even the first key is, the state stays as it is.
   const int qmax_wg = a.q_pos[min(q0 + BM - 1, Lq - 1)];
-  int T = (Lkv + BN - 1) / BN;
-  if (causal) {
-    int lo = 0, hi = T;  // first tile whose first key is past qmax_wg
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (kpos[mid * BN] <= qmax_wg) lo = mid + 1; else hi = mid;
-    }
-    T = lo;
-  }
-  if (T == 0) return;  // nothing visible: the state is unchanged
+  const int qmin_wg = a.q_pos[q0];
+  const int n_tiles = (Lkv + BN - 1) / BN;
+  if (causal && kpos[0] > qmax_wg) return;
 
   const int qmin_w = wave_active ? a.q_pos[q0w] : INT32_MAX;
   const int qmax_w = wave_active ? a.q_pos[min(q0w + 31, Lq - 1)] : INT32_MIN;
@@ -226,6 +256,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     }
   };
 
+  // The first tiles of the ping-pong loop are copied right away (clamped to
+  // the chunk; a tile past the range found below is copied but never used),
+  // then the query and state loads are issued, so that these round trips to
+  // memory overlap each other and the tile-range search that follows them.
+  // Whatever path runs next waits for the copies before its first barrier.
+  const bool p1_possible = fast_ok && (causal || !ALIBI) && Lkv >= BN;
+  if (p1_possible) {
+    dma_k(0, 0);
+    dma_k(1, min(1, n_tiles - 1) * BN);
+    dma_k(2, min(2, n_tiles - 1) * BN);
+    dma_v(0, 0);
+    dma_v(1, min(1, n_tiles - 1) * BN);
+  }
+
+  // Incoming m and l of this lane's row (unconditional loads through a
+  // buffer resource: rows past the end read 0 and are replaced below).
+  const auto rm = make_rsrc(mh, (int64_t)Lq * 4);
+  const auto rl = make_rsrc(lh, (int64_t)Lq * 4);
+  const float m_in = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, (uint32_t)row * 4, 0, 0));
+  const float l_in = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)row * 4, 0, 0));
+
   // Q fragments (B operand of S^T = K Q^T): lane holds query `row`, d slice
   // 16*kk + 8*hf .. +7.
   uint4 qf[KK];
@@ -233,8 +284,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   for (int kk = 0; kk < KK; ++kk) qf[kk] = buf_load16(rq, (uint32_t)(row * D + 16 * kk + 8 * hf) * 2);
 
   // Running state. O^T element (dt, e) of this lane is d = 32*dt + 8*(e/4) +
-  // 4*hf + e%4 of query `row`. m_ref: reference max for the exponents; m_max:
-  // true running max (both base 2). l per half-wave.
+  // 4*hf + e%4 of query `row`. m_ref: reference of the exponents (base 2).
+  // l per half-wave.
   ra_f32x16 O[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -247,10 +298,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       O[dt][4 * a4 + 3] = __uint_as_float(v.w);
     }
   }
-  float m_ref = row_ok ? mh[row] * RA_LOG2E : -INFINITY;
-  float m_max = m_ref;
-  float l_run = (row_ok && hf == 0) ? lh[row] : 0.0f;
+  float m_ref = row_ok ? m_in * RA_LOG2E : -INFINITY;
+  float l_run = (row_ok && hf == 0) ? l_in : 0.0f;
   bool touched = false;
+
+  // Tile range. T: tiles whose first key is at most the work-group's last
+  // query (all tiles without the causal mask). T1: leading complete tiles
+  // that every row of the work-group sees in full (their last key is at most
+  // its first query), taken by the ping-pong loop; T1 <= T.
+  int T = n_tiles, T1 = 0;
+  if (p1_possible) T1 = Lkv / BN;
+  if (causal) tile_counts(kpos, T, qmax_wg, p1_possible ? T1 : 0, qmin_wg, lane, T, T1);
 
   // V^T fragment for d tile dt and keys kb0 + 8*hf + 0..7 (two transposing reads).
   const int g16 = lane >> 4, j16 = lane & 15;
@@ -298,62 +356,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   };
 
   // Softmax of tile t in place: S -> P (bf16), lazy rescale of O and l.
-  auto softmax = [&](auto mode_tag, int buf, int kv0, auto cond_tag) {
+  // Scores in base 2: S*c for kFast, S (already scaled and biased) otherwise.
+  auto exps = [&](auto mode_tag, float off) {
     constexpr int MODE = decltype(mode_tag)::value;
-    constexpr bool COND = decltype(cond_tag)::value;
-    float rowc = 0.0f;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      if constexpr (MODE == kAlibiLinear) {
-        const float4* kbv = reinterpret_cast<const float4*>(&kb[buf][32 * sb + 8 * hf]);
-#pragma unroll
-        for (int e8 = 0; e8 < 2; ++e8) {
-          const float4 x0 = kbv[4 * e8], x1 = kbv[4 * e8 + 1];
-          const float kv8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) S[sb][8 * e8 + i] = fmaf(S[sb][8 * e8 + i], c, kv8[i]);
-        }
-      } else if constexpr (MODE == kExact) {
-        const int4* kpv = reinterpret_cast<const int4*>(&kp[buf][32 * sb + 8 * hf]);
-#pragma unroll
-        for (int e8 = 0; e8 < 2; ++e8) {
-          const int4 p0 = kpv[4 * e8], p1 = kpv[4 * e8 + 1];
-          const int kv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int j = 32 * sb + 16 * e8 + 8 * hf + i;
-            float x = S[sb][8 * e8 + i] * c;
-            if (ALIBI) x = fmaf(-sl2, (float)abs(my_pos - kv8[i]), x);
-            const bool vis = (kv0 + j < Lkv) && (!causal || kv8[i] <= my_pos);
-            S[sb][8 * e8 + i] = vis ? x : -INFINITY;
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, S[sb][e]);
-    }
-    tmax = fmaxf(tmax, ra_swap_halves(tmax));
-    if constexpr (MODE == kFast) {
-      tmax *= c;
-    } else if constexpr (MODE == kAlibiLinear) {
-      // bias = -slope*(pos_q - pos_k) = slope*(pos_k - base) - slope*(pos_q - base)
-      rowc = -sl2 * (float)(my_pos - uniform_i(kbase[buf]));
-      tmax += rowc;
-    }
-    m_max = fmaxf(m_max, tmax);
-    // Lazy rescale, branch-free: the reference only moves when a score
-    // exceeds it by more than 2^tau, so alpha is exactly 1 on almost every tile.
-    const float nref = tmax > m_ref + kTau ? fmaxf(m_ref, tmax) : m_ref;
-    const float alpha = nref == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - nref);
-    // Phase 1 skips the multiply when no lane of the wave moved its
-    // reference; the per-tile loop of phase 2 keeps it branch-free.
-    if (!COND || __builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
-    }
-    m_ref = nref;
-    const float off = rowc - (m_ref == -INFINITY ? 0.0f : m_ref);
     float psum = 0.0f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -373,26 +378,97 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
         P[sb][e >> 1] = ra_pack_bf16(p0, p1);
       }
     }
+    return psum;
+  };
+  // ALiBi terms of a fully visible tile (linear in the key position): per-key
+  // part added here, per-row constant returned.
+  auto alibi_linear = [&](int buf) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const float4* kbv = reinterpret_cast<const float4*>(&kb[buf][32 * sb + 8 * hf]);
+#pragma unroll
+      for (int e8 = 0; e8 < 2; ++e8) {
+        const float4 x0 = kbv[4 * e8], x1 = kbv[4 * e8 + 1];
+        const float kv8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S[sb][8 * e8 + i] = fmaf(S[sb][8 * e8 + i], c, kv8[i]);
+      }
+    }
+    // bias = -slope*(pos_q - pos_k) = slope*(pos_k - base) - slope*(pos_q - base)
+    return -sl2 * (float)(my_pos - uniform_i(kbase[buf]));
+  };
+  // Row max of the tile's scores (base 2), over both halves of the wave.
+  auto row_max = [&](auto mode_tag, float rowc) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, S[sb][e]);
+    tmax = fmaxf(tmax, ra_swap_halves(tmax));
+    return MODE == kFast ? tmax * c : tmax + rowc;
+  };
+  // Move the reference to the tile max when that exceeds it by more than
+  // 2^tau (always when it is -inf); rescale O; returns the factor for l.
+  auto move_ref = [&](float tmax, bool cond) {
+    const float nref = tmax > m_ref + kTau ? fmaxf(m_ref, tmax) : m_ref;
+    const float alpha = nref == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - nref);
+    if (!cond || __builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+    }
+    m_ref = nref;
+    return alpha;
+  };
+
+  // Fully visible tiles (ping-pong loop): exponents are first taken against
+  // the current reference with no row max at all. Only when some lane's sum
+  // of P leaves [0, kLimit] (its reference is -inf, or a score rose more
+  // than about log2(kLimit / 32) above it) does the wave take the tile max,
+  // move the reference and redo the exponents. Since 32 * 2^tau < kLimit, a
+  // tile that passes the check never had to move the reference.
+  auto softmax_fast = [&](auto mode_tag, int buf) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    const float rowc = MODE == kAlibiLinear ? alibi_linear(buf) : 0.0f;
+    float psum = exps(mode_tag, rowc - m_ref);
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kLimit))) {
+      const float alpha = move_ref(row_max(mode_tag, rowc), true);
+      psum = exps(mode_tag, rowc - (m_ref == -INFINITY ? 0.0f : m_ref));
+      l_run *= alpha;
+    }
+    l_run += psum;
+  };
+
+  // Any tile: masked per element where needed, with the row max.
+  auto softmax = [&](auto mode_tag, int buf, int kv0) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    float rowc = 0.0f;
+    if constexpr (MODE == kAlibiLinear) {
+      rowc = alibi_linear(buf);
+    } else if constexpr (MODE == kExact) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int4* kpv = reinterpret_cast<const int4*>(&kp[buf][32 * sb + 8 * hf]);
+#pragma unroll
+        for (int e8 = 0; e8 < 2; ++e8) {
+          const int4 p0 = kpv[4 * e8], p1 = kpv[4 * e8 + 1];
+          const int kv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int j = 32 * sb + 16 * e8 + 8 * hf + i;
+            float x = S[sb][8 * e8 + i] * c;
+            if (ALIBI) x = fmaf(-sl2, (float)abs(my_pos - kv8[i]), x);
+            const bool vis = (kv0 + j < Lkv) && (!causal || kv8[i] <= my_pos);
+            S[sb][8 * e8 + i] = vis ? x : -INFINITY;
+          }
+        }
+      }
+    }
+    const float alpha = move_ref(row_max(mode_tag, rowc), false);
+    const float psum = exps(mode_tag, rowc - (m_ref == -INFINITY ? 0.0f : m_ref));
     l_run = fmaf(l_run, alpha, psum);
   };
   constexpr int kUnmasked = ALIBI ? kAlibiLinear : kFast;
-
-  // Leading tiles that every row of the work-group sees in full (no mask, one
-  // code path for all eight waves), then the rest.
-  const int qmin_wg = a.q_pos[q0];
-  int T1 = 0;
-  if (fast_ok && (causal || !ALIBI)) {
-    T1 = Lkv / BN;  // complete tiles
-    if (causal) {
-      int lo = 0, hi = min(T1, T);  // first complete tile not entirely visible to qmin_wg
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (kpos[mid * BN + BN - 1] <= qmin_wg) lo = mid + 1; else hi = mid;
-      }
-      T1 = lo;
-    }
-    T1 = min(T1, T);
-  }
 
   // A work-group barrier that the compiler may not move any instruction
   // across, so that each set's MFMA and softmax phases stay where they are.
@@ -412,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(P[sb][i]));
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+v"(O[dt]));
-    asm volatile("" : "+v"(l_run), "+v"(m_ref), "+v"(m_max));
+    asm volatile("" : "+v"(l_run), "+v"(m_ref));
   };
   auto pin_mfma = [&]() {
 #pragma unroll
@@ -431,16 +507,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     // waited for at the end of its following softmax phase.
     touched = true;
     // Three K and three V buffers; tile u lives in buffer u % 3. K(0..2) and
-    // V(0..1) are loaded up front (clamped to the last phase-1 tile).
-    dma_k(0, 0);
-    dma_k(1, min(1, T1 - 1) * BN);
-    dma_k(2, min(2, T1 - 1) * BN);
-    dma_v(0, 0);
-    dma_v(1, min(1, T1 - 1) * BN);
+    // V(0..1) were copied up front.
     if constexpr (ALIBI) {
       store_kp(0, 0, load_kp(0));
-      store_kp(1, min(1, T1 - 1) * BN, load_kp(min(1, T1 - 1) * BN));
-      store_kp(2, min(2, T1 - 1) * BN, load_kp(min(2, T1 - 1) * BN));
+      store_kp(1, min(1, n_tiles - 1) * BN, load_kp(min(1, n_tiles - 1) * BN));
+      store_kp(2, min(2, n_tiles - 1) * BN, load_kp(min(2, n_tiles - 1) * BN));
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -452,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     int b0 = 0, b1 = 1, b2 = 2;
 #pragma clang loop unroll(disable)
     for (int t = 0; t < T1; ++t) {
-      softmax(std::integral_constant<int, kUnmasked>{}, b0, t * BN, std::true_type{});
+      softmax_fast(std::integral_constant<int, kUnmasked>{}, b0);
       pin_softmax();
       phase_barrier();
       __builtin_amdgcn_s_setprio(1);
@@ -516,9 +587,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
         qk_mfma(buf);
         const bool masked = (kv0 + BN > Lkv) || (causal && klast > qmin_w) || !fast_ok;
         if (masked || (ALIBI && !causal))
-          softmax(std::integral_constant<int, kExact>{}, buf, kv0, std::false_type{});
+          softmax(std::integral_constant<int, kExact>{}, buf, kv0);
         else
-          softmax(std::integral_constant<int, kUnmasked>{}, buf, kv0, std::false_type{});
+          softmax(std::integral_constant<int, kUnmasked>{}, buf, kv0);
         pv_mfma(buf);
       }
       if (!have_next) break;
@@ -529,20 +600,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   }
 
   if (!touched) return;
-  // Renormalise to the true running max and write the state back.
-  float l_tot = l_run + ra_swap_halves(l_run);
-  const float fac = m_max == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_max);
-  l_tot *= fac;
+  // Write the state back, taken against the reference.
+  const float l_tot = l_run + ra_swap_halves(l_run);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      buf_store16(ro, (uint32_t)(row * D + 32 * dt + 8 * a4 + 4 * hf) * 4, O[dt][4 * a4 + 0] * fac,
-                  O[dt][4 * a4 + 1] * fac, O[dt][4 * a4 + 2] * fac, O[dt][4 * a4 + 3] * fac);
+      buf_store16(ro, (uint32_t)(row * D + 32 * dt + 8 * a4 + 4 * hf) * 4, O[dt][4 * a4 + 0],
+                  O[dt][4 * a4 + 1], O[dt][4 * a4 + 2], O[dt][4 * a4 + 3]);
     }
   }
   if (row_ok && hf == 0) {
-    mh[row] = m_max * RA_LN2;
+    mh[row] = m_ref * RA_LN2;
     lh[row] = l_tot;
   }
 }
