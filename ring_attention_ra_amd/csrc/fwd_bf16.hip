@@ -34,11 +34,15 @@
 //    of the next tile and the P.V product of the current one; its LDS
 //    fragment reads run four MFMAs ahead of use, and the wave raises its
 //    issue priority for the phase so that its MFMAs and reads are not held
-//    behind the other wave's VALU work. K and V have three LDS
-//    buffers each: at the end of its MFMA phase for tile t every wave copies
-//    its share of K(t+3) and V(t+2) into the buffers that tiles t and t-1
-//    leave, and waits for its previous step's copies before the barrier, so
-//    a copy has two phases to land. The copies are issued from inline
+//    behind the other wave's VALU work. The fragments of the first four QK
+//    products are read at the start of the wave's preceding softmax phase,
+//    so the MFMA phase opens with a product instead of an LDS round trip.
+//    K has four LDS buffers and V three: at the end of its MFMA phase for
+//    tile t every wave copies its share of K(t+4) and V(t+2) into the
+//    buffers that tiles t and t-1 leave, and waits for its previous step's
+//    copies before the barrier, so a copy has two phases to land and a K
+//    tile is published a full phase before its first fragments are read
+//    early. The copies are issued from inline
 //    assembly, invisible to the compiler's wait insertion, so fragment reads
 //    of the other buffers go ahead while they fly. Empty volatile asm
 //    statements pin each phase's results and scheduling barriers keep the
@@ -108,9 +112,10 @@ __device__ __forceinline__ void interleave_qk_step() {
     interleave_qk_step<NQK, NPV, I + 1>();
   }
 }
+// The same pattern when the fragments of products 0..3 are already in
+// registers: the phase opens with its first MFMA.
 template <int NQK, int NPV>
-__device__ __forceinline__ void interleave_qk_first() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of QK products 0..3
+__device__ __forceinline__ void interleave_qk_rest() {
   interleave_qk_step<NQK, NPV, 0>();
 }
 
@@ -156,11 +161,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   constexpr int SLOTS = BN * CPR;       // 16-byte slots in a K (or V) tile
   constexpr int DMA_PER_WAVE = SLOTS / (kWaves * 64);
 
-  __shared__ uint4 Ks[3][SLOTS];
+  __shared__ uint4 Ks[4][SLOTS];
   __shared__ uint4 Vs[3][SLOTS];
-  __shared__ __align__(16) int kp[3][BN];
-  __shared__ __align__(16) float kb[ALIBI ? 3 : 1][BN];
-  __shared__ int kbase[3];  // position of the first key of the tile in kb[]
+  __shared__ __align__(16) int kp[4][BN];
+  __shared__ __align__(16) float kb[ALIBI ? 4 : 1][BN];
+  __shared__ int kbase[4];  // position of the first key of the tile in kb[]
 
   const int Lq = a.len_q, Lkv = a.len_kv;
   const int BH = a.batch * a.heads_q;
@@ -343,14 +348,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       }
     }
   };
+  auto k_frag = [&](int kbuf, int sb, int kk) {
+    const int krow = 32 * sb + perm_row(l32);
+    return Ks[kbuf][krow * CPR + ((2 * kk + hf) ^ k_swz(krow))];
+  };
   auto qk_mfma = [&](int kbuf) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       ra_f32x16 acc = ra_f32x16{};
-      const int krow = 32 * sb + perm_row(l32);
-      const int sw = k_swz(krow);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) acc = ra_mfma32(Ks[kbuf][krow * CPR + ((2 * kk + hf) ^ sw)], qf[kk], acc);
+      for (int kk = 0; kk < KK; ++kk) acc = ra_mfma32(k_frag(kbuf, sb, kk), qf[kk], acc);
+      S[sb] = acc;
+    }
+  };
+  // The same product with the fragments of its first kPre MFMAs already in
+  // registers (read at the start of the preceding softmax phase).
+  constexpr int kPre = 4;
+  uint4 kpre[kPre];
+  auto qk_mfma_pre = [&](int kbuf) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      ra_f32x16 acc = ra_f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        acc = ra_mfma32(sb * KK + kk < kPre ? kpre[sb * KK + kk] : k_frag(kbuf, sb, kk), qf[kk], acc);
       S[sb] = acc;
     }
   };
@@ -506,12 +527,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     // issues the copies at the start of its MFMA phase u: K(u+1) and V(u),
     // waited for at the end of its following softmax phase.
     touched = true;
-    // Three K and three V buffers; tile u lives in buffer u % 3. K(0..2) and
-    // V(0..1) were copied up front.
+    // Four K and three V buffers; K tile u lives in K buffer u % 4, V tile u
+    // in V buffer u % 3. K(0..2) and V(0..1) were copied up front, K(3) now.
+    dma_k(3, min(3, n_tiles - 1) * BN);
     if constexpr (ALIBI) {
-      store_kp(0, 0, load_kp(0));
-      store_kp(1, min(1, n_tiles - 1) * BN, load_kp(min(1, n_tiles - 1) * BN));
-      store_kp(2, min(2, n_tiles - 1) * BN, load_kp(min(2, n_tiles - 1) * BN));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) store_kp(u, min(u, n_tiles - 1) * BN, load_kp(min(u, n_tiles - 1) * BN));
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -519,42 +540,57 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     qk_mfma(0);
     pin_mfma();
     phase_barrier();
-    // Buffers of tiles t, t+1, t+2 (rotating).
-    int b0 = 0, b1 = 1, b2 = 2;
+    // K buffers of tiles t .. t+3 and V buffers of tiles t-1 .. t+1 (rotating).
+    int k0 = 0, k1 = 1, k2 = 2, k3 = 3;
+    int v0 = 0, v1 = 1, v2 = 2;
 #pragma clang loop unroll(disable)
     for (int t = 0; t < T1; ++t) {
-      softmax_fast(std::integral_constant<int, kUnmasked>{}, b0);
+      // First fragments of the next QK product, read before the softmax so
+      // that their latency hides behind it. K(t+1) was copied four phases ago
+      // and every wave has waited for its share of it before a barrier that
+      // both sets have passed since, so the reads may run ahead of the MFMA
+      // phase.
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) kpre[i] = k_frag(k1, i / KK, i % KK);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_fast(std::integral_constant<int, kUnmasked>{}, k0);
       pin_softmax();
       phase_barrier();
       __builtin_amdgcn_s_setprio(1);
-      qk_mfma(b1);  // the last one reads a stale tile and is discarded
-      pv_mfma(b0);
-      // LDS fragment reads four MFMAs ahead of use.
-      interleave_qk_first<2 * KK, 4 * DT>();
-      // Copies two tiles ahead, issued after this phase's fragment reads:
-      // K(t+3) into the buffer K(t) leaves, V(t+2) into the one V(t-1) left
-      // (clamped to the last phase-1 tile). Every reader of those buffers
-      // has passed a barrier since. This wave's copies of the previous step
-      // must land before the barrier; this step's may stay in flight.
-      dma_p1(b0, min(t + 3, T1 - 1) * BN, b2, min(t + 2, T1 - 1) * BN);
+      qk_mfma_pre(k1);  // the last one reads a stale tile and is discarded
+      pv_mfma(v0);
+      // LDS fragment reads four MFMAs ahead of use (those of the first four
+      // are in registers already).
+      interleave_qk_rest<2 * KK, 4 * DT>();
+      // Copies: K(t+4) into the buffer K(t) leaves, V(t+2) into the one
+      // V(t-1) left (clamped to the last phase-1 tile). Every reader of those
+      // buffers has passed a barrier since. This wave's copies of the
+      // previous step must land before the barrier; this step's may stay in
+      // flight.
+      dma_p1(k0, min(t + 4, T1 - 1) * BN, v2, min(t + 2, T1 - 1) * BN);
       pin_mfma();
       __builtin_amdgcn_s_setprio(0);
       // s_waitcnt vmcnt(n), n = this step's copies (expcnt and lgkmcnt fields
       // at their maximum: no wait; vmcnt in bits 3:0).
       if (ALIBI && wave == 0) {
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_PER_WAVE + 1));
-        // Key positions of tile t+2 have landed: its ALiBi terms.
-        const int kpv = kp[b2][lane], k0 = kp[b2][0];
-        kb[b2][lane] = sl2 * (float)(kpv - k0);
-        if (lane == 0) kbase[b2] = k0;
+        // Key positions of tile t+3 have landed: its ALiBi terms.
+        const int kpv = kp[k3][lane], kf = kp[k3][0];
+        kb[k3][lane] = sl2 * (float)(kpv - kf);
+        if (lane == 0) kbase[k3] = kf;
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_PER_WAVE));
       }
       phase_barrier();
-      const int bn = b0;
-      b0 = b1;
-      b1 = b2;
-      b2 = bn;
+      const int kn = k0;
+      k0 = k1;
+      k1 = k2;
+      k2 = k3;
+      k3 = kn;
+      const int vn = v0;
+      v0 = v1;
+      v1 = v2;
+      v2 = vn;
     }
     if (set == 0) phase_barrier();
   }
