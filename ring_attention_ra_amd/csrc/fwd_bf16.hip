@@ -34,9 +34,10 @@
 //    of the next tile and the P.V product of the current one; its LDS
 //    fragment reads run four MFMAs ahead of use, and the wave raises its
 //    issue priority for the phase so that its MFMAs and reads are not held
-//    behind the other wave's VALU work. The fragments of the first four QK
-//    products are read at the start of the wave's preceding softmax phase,
-//    so the MFMA phase opens with a product instead of an LDS round trip.
+//    behind the other wave's VALU work. Without ALiBi, the fragments of the
+//    first four QK products are read at the start of the wave's preceding
+//    softmax phase, so the MFMA phase opens with a product instead of an LDS
+//    round trip.
 //    K has four LDS buffers and V three: at the end of its MFMA phase for
 //    tile t every wave copies its share of K(t+4) and V(t+2) into the
 //    buffers that tiles t and t-1 leave, and waits for its previous step's
@@ -52,7 +53,8 @@
 //    per-element masks where needed.
 //  * The output is rescaled lazily: exponents are taken against a reference
 //    that is raised to the tile max (and O, l rescaled) only when the scores
-//    outgrow it. Over the fully visible tiles no row max is taken at all: the
+//    outgrow it. Over the fully visible tiles without ALiBi no row max is
+//    taken at all: the
 //    exponentials are computed against the reference first, and only when a
 //    lane's sum of P exceeds 2^14 (or the reference is still -inf) does the
 //    wave take the max, move the reference and redo them, so P stays below
@@ -116,6 +118,13 @@ __device__ __forceinline__ void interleave_qk_step() {
 // registers: the phase opens with its first MFMA.
 template <int NQK, int NPV>
 __device__ __forceinline__ void interleave_qk_rest() {
+  interleave_qk_step<NQK, NPV, 0>();
+}
+// The pattern when the phase has to read those fragments itself: they go
+// first.
+template <int NQK, int NPV>
+__device__ __forceinline__ void interleave_qk_first() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of QK products 0..3
   interleave_qk_step<NQK, NPV, 0>();
 }
 
@@ -442,22 +451,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     return alpha;
   };
 
-  // Fully visible tiles (ping-pong loop): exponents are first taken against
-  // the current reference with no row max at all. Only when some lane's sum
+  // Fully visible tiles without ALiBi (ping-pong loop): exponents are first
+  // taken against the current reference with no row max at all. Only when some lane's sum
   // of P leaves [0, kLimit] (its reference is -inf, or a score rose more
   // than about log2(kLimit / 32) above it) does the wave take the tile max,
   // move the reference and redo the exponents. Since 32 * 2^tau < kLimit, a
   // tile that passes the check never had to move the reference.
+  // Under ALiBi the bias rises by about slope * 64 from one tile to the next
+  // as the keys approach the queries, so on the steep heads the check would
+  // fail on almost every tile and the exponentials would run twice: those
+  // tiles take the row max first and move the reference lazily (by 2^tau).
   auto softmax_fast = [&](auto mode_tag, int buf) {
     constexpr int MODE = decltype(mode_tag)::value;
-    const float rowc = MODE == kAlibiLinear ? alibi_linear(buf) : 0.0f;
-    float psum = exps(mode_tag, rowc - m_ref);
-    if (__builtin_amdgcn_ballot_w64(!(psum <= kLimit))) {
+    if constexpr (MODE == kAlibiLinear) {
+      const float rowc = alibi_linear(buf);
       const float alpha = move_ref(row_max(mode_tag, rowc), true);
-      psum = exps(mode_tag, rowc - (m_ref == -INFINITY ? 0.0f : m_ref));
-      l_run *= alpha;
+      l_run = fmaf(l_run, alpha, exps(mode_tag, rowc - (m_ref == -INFINITY ? 0.0f : m_ref)));
+    } else {
+      float psum = exps(mode_tag, -m_ref);
+      if (__builtin_amdgcn_ballot_w64(!(psum <= kLimit))) {
+        const float alpha = move_ref(row_max(mode_tag, 0.0f), true);
+        psum = exps(mode_tag, m_ref == -INFINITY ? 0.0f : -m_ref);
+        l_run *= alpha;
+      }
+      l_run += psum;
     }
-    l_run += psum;
   };
 
   // Any tile: masked per element where needed, with the row max.
@@ -550,18 +568,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       // and every wave has waited for its share of it before a barrier that
       // both sets have passed since, so the reads may run ahead of the MFMA
       // phase.
+      // Under ALiBi the softmax opens with LDS reads of the per-key bias; the
+      // early reads would delay them (LDS reads complete in order), so that
+      // variant reads all its fragments in the MFMA phase.
+      if constexpr (!ALIBI) {
 #pragma unroll
-      for (int i = 0; i < kPre; ++i) kpre[i] = k_frag(k1, i / KK, i % KK);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < kPre; ++i) kpre[i] = k_frag(k1, i / KK, i % KK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       softmax_fast(std::integral_constant<int, kUnmasked>{}, k0);
       pin_softmax();
       phase_barrier();
       __builtin_amdgcn_s_setprio(1);
-      qk_mfma_pre(k1);  // the last one reads a stale tile and is discarded
-      pv_mfma(v0);
-      // LDS fragment reads four MFMAs ahead of use (those of the first four
-      // are in registers already).
-      interleave_qk_rest<2 * KK, 4 * DT>();
+      // The last QK reads a stale tile and is discarded. LDS fragment reads
+      // run four MFMAs ahead of use.
+      if constexpr (!ALIBI) {
+        qk_mfma_pre(k1);
+        pv_mfma(v0);
+        interleave_qk_rest<2 * KK, 4 * DT>();
+      } else {
+        qk_mfma(k1);
+        pv_mfma(v0);
+        interleave_qk_first<2 * KK, 4 * DT>();
+      }
       // Copies: K(t+4) into the buffer K(t) leaves, V(t+2) into the one
       // V(t-1) left (clamped to the last phase-1 tile). Every reader of those
       // buffers has passed a barrier since. This wave's copies of the
