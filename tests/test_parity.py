@@ -142,6 +142,16 @@ def test_fwd_bf16_variants(d, layout, causal, alibi, hq, hkv, n, c):
     _check_full(Case("bf16", 1, hq, hkv, d, n * c, n, layout, causal, alibi, seed=21))
 
 
+@pytest.mark.parametrize("layout,causal,alibi,hq,hkv,n,c", [
+    ("zigzag", True, False, 2, 2, 4, 40),          # chunk shorter than one 64-key tile
+    ("contiguous", True, False, 1, 1, 2, 4497),    # 71 key tiles: two rounds of the tile search, ragged
+    ("zigzag", True, False, 2, 2, 2, 4497),
+    ("zigzag", True, True, 2, 1, 2, 4497),         # ALiBi + GQA over the same range
+])
+def test_fwd_bf16_tile_range_edges(layout, causal, alibi, hq, hkv, n, c):
+    _check_full(Case("bf16", 1, hq, hkv, 128, n * c, n, layout, causal, alibi, seed=25))
+
+
 def test_fwd_bf16_batch2_and_std():
     _check_full(Case("bf16", 2, 3, 1, 128, 4 * 256, 4, "zigzag", True, True, std=0.7, seed=23))
 
