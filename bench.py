@@ -7,6 +7,13 @@ in ring order, ra_finalize, and -- for the workloads that have one -- the
 backward ring (ra_bwd_delta + one ra_step_bwd per chunk). Inputs are seeded
 synthetic tensors already resident in HBM when the timed region starts.
 
+The rank permutes its own Q, K and V chunks on the launch stream. The K/V
+chunks of the other ranks -- in a real ring each permuted by its owner at the
+same time and then received -- are permuted on a second stream (default
+priority), each while the step before the one that uses it runs; each step
+waits for its chunk's event. --serial-permute runs every permutation on the launch
+stream before the first step instead.
+
 Prints one JSON line. `value` is causal-effective TFLOP/s of the whole step
 (forward 4*D FLOP per visible (query, key) pair per query head, backward
 10*D). `roofline` is the dominant kernel (the bf16 step kernel) timed live
@@ -61,6 +68,8 @@ def parse():
     ap.add_argument("--workload", default=str(configs.HEADLINE.index),
                     help="workload index (1-6) or name; default: the 128K zig-zag share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial-permute", action="store_true",
+                    help="permute every K/V chunk on the launch stream before the first step")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows in the CPU-baseline sample")
     ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-baseline sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fwd_bf16_128k_zigzag_traffic.json"),
@@ -143,23 +152,45 @@ def main():
     sched = ring.ring_schedule(n, w.rank)
     stream = torch.cuda.current_stream()
 
-    fwd_events, bwd_events, perm_events = [], [], []
+    side = torch.cuda.Stream(device=dev)  # default priority
+    fwd_events, bwd_events, perm_events, side_events = [], [], [], []
 
-    def ev():
+    def ev(on=None):
         e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
+        e.record(stream if on is None else on)
         return e
 
     def step(timed):
+        ready = {}
         if timed:
             perm_events.append(ev())
         _lib.ra_layout_permute(q_g, q_loc, None, b * hq, s, d, n, w.layout, rank=w.rank)
-        _lib.ra_layout_permute(k_g, k_ch, pos, b * hkv, s, d, n, w.layout, rank=-1)
-        _lib.ra_layout_permute(v_g, v_ch, None, b * hkv, s, d, n, w.layout, rank=-1)
+        if args.serial_permute:
+            _lib.ra_layout_permute(k_g, k_ch, pos, b * hkv, s, d, n, w.layout, rank=-1)
+            _lib.ra_layout_permute(v_g, v_ch, None, b * hkv, s, d, n, w.layout, rank=-1)
+        else:
+            _lib.ra_layout_permute(k_g, k_ch[w.rank], pos[w.rank], b * hkv, s, d, n, w.layout, rank=w.rank)
+            _lib.ra_layout_permute(v_g, v_ch[w.rank], None, b * hkv, s, d, n, w.layout, rank=w.rank)
         if timed:
             perm_events.append(ev())
         _lib.ra_state_init(dims, o_acc, m, l)
-        for src in sched:
+        for j, src in enumerate(sched):
+            if j > 0 and not args.serial_permute:
+                stream.wait_event(ready[src])
+            if not args.serial_permute and j + 1 < n:
+                # The next chunk in ring order is permuted on the side stream
+                # while this step runs, the way it would arrive during it. It
+                # starts once every earlier use of its buffers (all on the
+                # launch stream) is behind it.
+                nxt = sched[j + 1]
+                side.wait_event(ev())
+                if timed:
+                    side_events.append(ev(side))
+                _lib.ra_layout_permute(k_g, k_ch[nxt], pos[nxt], b * hkv, s, d, n, w.layout, rank=nxt, stream=side)
+                _lib.ra_layout_permute(v_g, v_ch[nxt], None, b * hkv, s, d, n, w.layout, rank=nxt, stream=side)
+                ready[nxt] = ev(side)
+                if timed:
+                    side_events.append(ready[nxt])
             if timed:
                 fwd_events.append(ev())
             _lib.ra_step_fwd(dims, q_loc, k_ch[src], v_ch[src], pos[w.rank], pos[src], w.causal, w.scale,
@@ -204,7 +235,13 @@ def main():
     fwd_total_ms = sum(fwd_ms) / args.steps
     fwd_tflops = fwd_flops / (fwd_total_ms * 1e-3) / 1e12
     perm_ms = sum(pair_ms(perm_events)) / args.steps
-    perm_bytes = 2.0 * (q_loc.numel() + k_ch.numel() + v_ch.numel()) * q_loc.element_size() + pos.numel() * 4
+    esz = q_loc.element_size()
+    if args.serial_permute:
+        perm_bytes = 2.0 * (q_loc.numel() + k_ch.numel() + v_ch.numel()) * esz + pos.numel() * 4
+    else:
+        perm_bytes = 2.0 * (q_loc.numel() + k_ch[0].numel() + v_ch[0].numel()) * esz + pos[0].numel() * 4
+        side_ms = sum(pair_ms(side_events)) / args.steps
+        side_bytes = 2.0 * (n - 1) * (k_ch[0].numel() + v_ch[0].numel()) * esz + (n - 1) * pos[0].numel() * 4
 
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
@@ -222,9 +259,16 @@ def main():
         "step_kernel_ms_per_step": round(fwd_total_ms, 4),
         "permute_ms_per_step": round(perm_ms, 4),
         "permute_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
+        "permute_scope": "every chunk, launch stream" if args.serial_permute else "own Q/K/V chunks, launch stream",
         "visible_pairs_per_head": sum(pairs),
         "fwd_flop_per_step": fwd_flops,
     }
+    if not args.serial_permute:
+        # The other ranks' chunks on the side stream, one per step, each
+        # overlapped with a step (so not a rate of its own).
+        extra["permute_other_ranks"] = {"stream": "side, overlapped with the steps",
+                                        "ms_per_step": round(side_ms, 4),
+                                        "gbs_while_overlapped": round(side_bytes / (side_ms * 1e-3) / 1e9, 1)}
     # Rotary position embedding of the rank's K chunks (every chunk by its own
     # global positions), out of place, as a separate HBM-bound pass: not part
     # of the step above, timed after it with HIP events on the same stream.
