@@ -42,7 +42,7 @@ extern "C" {
 typedef enum ra_status {
   RA_OK = 0,
   RA_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, negative size, bad enum, inconsistent shape */
-  RA_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (e.g. head_dim) */
+  RA_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement (e.g. head_dim) */
   RA_ERR_HIP = 3               /* the HIP runtime reported an error on launch */
 } ra_status;
 
