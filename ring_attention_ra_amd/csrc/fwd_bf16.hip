@@ -37,7 +37,9 @@
 //    behind the other wave's VALU work. Without ALiBi, the fragments of the
 //    first four QK products are read at the start of the wave's preceding
 //    softmax phase, so the MFMA phase opens with a product instead of an LDS
-//    round trip.
+//    round trip. Under ALiBi (with the causal mask) the QK accumulators of a
+//    fully visible tile start from its per-key bias term divided by
+//    scale * log2 e, so the softmax adds only a per-row constant.
 //    K has four LDS buffers and V three: at the end of its MFMA phase for
 //    tile t every wave copies its share of K(t+4) and V(t+2) into the
 //    buffers that tiles t and t-1 leave, and waits for its previous step's
@@ -67,8 +69,9 @@
 //  * Key tiles past the last query of the work-group are never visited
 //    (positions increase); a wave skips tiles entirely in its causal future.
 //    Under the causal mask the ALiBi term of a fully visible tile is linear
-//    in the key position, so it becomes one per-key term staged in LDS plus
-//    one per-row constant.
+//    in the key position, so it becomes one per-key term staged in LDS (the
+//    start value of the QK accumulators in the ping-pong loop) plus one
+//    per-row constant.
 //  * Work-groups are ordered heaviest-first and, when the counts allow, each
 //    XCD is given whole heads so that its L2 serves one head's K/V stream.
 //  * LDS rows are XOR-swizzled in 16-byte units so that the fragment reads of
@@ -122,9 +125,10 @@ __device__ __forceinline__ void interleave_qk_rest() {
 }
 // The pattern when the phase has to read those fragments itself: they go
 // first.
-template <int NQK, int NPV>
+template <int NQK, int NPV, int N0 = 4>
 __device__ __forceinline__ void interleave_qk_first() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of QK products 0..3
+  // reads of QK products 0..3 (and of the accumulator start values, if any)
+  __builtin_amdgcn_sched_group_barrier(0x100, N0, 0);
   interleave_qk_step<NQK, NPV, 0>();
 }
 
@@ -174,6 +178,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   __shared__ uint4 Vs[3][SLOTS];
   __shared__ __align__(16) int kp[4][BN];
   __shared__ __align__(16) float kb[ALIBI ? 4 : 1][BN];
+  // The same per-key term divided by scale * log2 e: the start value of the
+  // tile's QK accumulators in the ping-pong loop.
+  __shared__ __align__(16) float kbc[ALIBI ? 4 : 1][BN];
   __shared__ int kbase[4];  // position of the first key of the tile in kb[]
 
   const int Lq = a.len_q, Lkv = a.len_kv;
@@ -220,6 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   const float c = a.scale * RA_LOG2E;
   const bool fast_ok = c > 0.0f;
   const float sl2 = ALIBI ? a.slopes[h] * RA_LOG2E : 0.0f;
+  const float sl2c = ALIBI ? a.slopes[h] / a.scale : 0.0f;
 
   // ---- tile movement ----
   // Phase-1 copies: every wave moves DMA_PER_WAVE 16-byte slots of a K
@@ -265,6 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       if constexpr (ALIBI) {
         const int k0 = kpos[kv0];
         kb[buf][tid] = sl2 * (float)(kpv - k0);
+        kbc[buf][tid] = sl2c * (float)(kpv - k0);
         if (tid == 0) kbase[buf] = k0;
       }
     }
@@ -370,6 +379,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       S[sb] = acc;
     }
   };
+  // Under ALiBi, over the fully visible tiles: the accumulators start from
+  // the tile's per-key term / (scale * log2 e), so that S * c comes out with
+  // the key part of the bias already added.
+  auto qk_mfma_bias = [&](int kbuf) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const float4* kv = reinterpret_cast<const float4*>(&kbc[kbuf][32 * sb + 8 * hf]);
+      const float4 x0 = kv[0], x1 = kv[1], x2 = kv[4], x3 = kv[5];
+      ra_f32x16 acc = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                       x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) acc = ra_mfma32(k_frag(kbuf, sb, kk), qf[kk], acc);
+      S[sb] = acc;
+    }
+  };
   // The same product with the fragments of its first kPre MFMAs already in
   // registers (read at the start of the preceding softmax phase).
   constexpr int kPre = 4;
@@ -410,8 +434,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     }
     return psum;
   };
-  // ALiBi terms of a fully visible tile (linear in the key position): per-key
-  // part added here, per-row constant returned.
+  // ALiBi terms of a fully visible tile outside the ping-pong loop (linear in
+  // the key position): per-key part added here, per-row constant returned.
   auto alibi_linear = [&](int buf) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -464,9 +488,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   auto softmax_fast = [&](auto mode_tag, int buf) {
     constexpr int MODE = decltype(mode_tag)::value;
     if constexpr (MODE == kAlibiLinear) {
-      const float rowc = alibi_linear(buf);
-      const float alpha = move_ref(row_max(mode_tag, rowc), true);
-      l_run = fmaf(l_run, alpha, exps(mode_tag, rowc - (m_ref == -INFINITY ? 0.0f : m_ref)));
+      // S holds scores / c with the key part of the bias (qk_mfma_bias); the
+      // row part is a constant per lane.
+      const float rowc = -sl2 * (float)(my_pos - uniform_i(kbase[buf]));
+      const float alpha = move_ref(row_max(std::integral_constant<int, kFast>{}, 0.0f) + rowc, true);
+      l_run = fmaf(l_run, alpha,
+                   exps(std::integral_constant<int, kFast>{}, rowc - (m_ref == -INFINITY ? 0.0f : m_ref)));
     } else {
       float psum = exps(mode_tag, -m_ref);
       if (__builtin_amdgcn_ballot_w64(!(psum <= kLimit))) {
@@ -555,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (set == 1) phase_barrier();
-    qk_mfma(0);
+    if constexpr (ALIBI) qk_mfma_bias(0); else qk_mfma(0);
     pin_mfma();
     phase_barrier();
     // K buffers of tiles t .. t+3 and V buffers of tiles t-1 .. t+1 (rotating).
@@ -568,9 +595,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       // and every wave has waited for its share of it before a barrier that
       // both sets have passed since, so the reads may run ahead of the MFMA
       // phase.
-      // Under ALiBi the softmax opens with LDS reads of the per-key bias; the
-      // early reads would delay them (LDS reads complete in order), so that
-      // variant reads all its fragments in the MFMA phase.
+      // The ALiBi variant reads its fragments, and its accumulators' start
+      // values, in the MFMA phase: the early reads measured 1% slower there.
       if constexpr (!ALIBI) {
 #pragma unroll
         for (int i = 0; i < kPre; ++i) kpre[i] = k_frag(k1, i / KK, i % KK);
@@ -587,9 +613,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
         pv_mfma(v0);
         interleave_qk_rest<2 * KK, 4 * DT>();
       } else {
-        qk_mfma(k1);
+        qk_mfma_bias(k1);
         pv_mfma(v0);
-        interleave_qk_first<2 * KK, 4 * DT>();
+        interleave_qk_first<2 * KK, 4 * DT, 12>();
       }
       // Copies: K(t+4) into the buffer K(t) leaves, V(t+2) into the one
       // V(t-1) left (clamped to the last phase-1 tile). Every reader of those
@@ -605,7 +631,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_PER_WAVE + 1));
         // Key positions of tile t+3 have landed: its ALiBi terms.
         const int kpv = kp[k3][lane], kf = kp[k3][0];
-        kb[k3][lane] = sl2 * (float)(kpv - kf);
+        kbc[k3][lane] = sl2c * (float)(kpv - kf);
         if (lane == 0) kbase[k3] = kf;
       } else {
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DMA_PER_WAVE));
