@@ -95,6 +95,10 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
   __shared__ __align__(16) float lse_s[2][TROWS];
   __shared__ __align__(16) float del_s[2][TROWS];
   __shared__ __align__(16) int qp_s[2][TROWS];
+  // Under ALiBi: -(lse * log2 e + slope * log2 e * (q_pos - first query of
+  // the item)) / (scale * log2 e) per query row, the start value of S on the
+  // items a key block sees in full.
+  __shared__ __align__(16) float lsec_s[ALIBI ? 2 : 1][TROWS];
   // P of the current tile, handed from each key block's dV wave to its dK
   // wave: [key block][query half][element quad][lane], 4 floats each.
   __shared__ float4 Px[4][2][4][64];
@@ -165,23 +169,29 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
       tc.copy(Qs[buf], static_cast<const uint16_t*>(a.q) + qhead * Lq * D, q0, Lq, kb, lane);
       tc.copy(Os[buf], static_cast<const uint16_t*>(a.d_o) + qhead * Lq * D, q0, Lq, kb, lane);
     };
-    struct RowVals { float lse, del; int qp; };
+    struct RowVals { float lse, del, sl2; int qp, qb; };
     auto load_rows = [&](int it) {
-      RowVals r{0.f, 0.f, 0};
+      RowVals r{0.f, 0.f, 0.f, 0, 0};
       if (tid < TROWS) {
         const int hq = item_head(it), q = min(item_q0(it) + tid, Lq - 1);
         const int64_t row = ((int64_t)b * a.heads_q + hq) * Lq + q;
         r.lse = a.lse[row];  // converted when stored: no use before the loop's end
         r.del = a.delta[row];
         r.qp = a.q_pos[q];
+        if constexpr (ALIBI) {
+          r.sl2 = a.slopes[hq] * RA_LOG2E;
+          r.qb = a.q_pos[item_q0(it)];
+        }
       }
       return r;
     };
     auto store_rows = [&](int buf, const RowVals& r) {
       if (tid < TROWS) {
-        lse_s[buf][tid] = safe_lse2(r.lse);
+        const float l2 = safe_lse2(r.lse);
+        lse_s[buf][tid] = l2;
         del_s[buf][tid] = r.del;
         qp_s[buf][tid] = r.qp;
+        if constexpr (ALIBI) lsec_s[buf][tid] = -(l2 + r.sl2 * (float)(r.qp - r.qb)) / c;
       }
     };
 
@@ -216,11 +226,10 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
     };
     // One 32-query block's product A(rows) x bf^T: S (dV wave) or dP (dK wave).
     constexpr int LA = 3;
-    auto row_product = [&](const uint4* tile, int qb) {
+    auto row_product = [&](const uint4* tile, int qb, ra_f32x16 r) {
       uint4 fr[LA + 1];
 #pragma unroll
       for (int kk = 0; kk < LA; ++kk) fr[kk] = row_frag(tile, 32 * qb, kk);
-      ra_f32x16 r = ra_f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         if (kk + LA < KK) fr[(kk + LA) % (LA + 1)] = row_frag(tile, 32 * qb, kk + LA);
@@ -259,7 +268,11 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
       const int qfirst = uniform_i(qp_s[buf][0]);
       const int qlast = uniform_i(qp_s[buf][TROWS - 1]);
       const bool active = wave_active && !(causal && qlast < kmin_w);
-      const bool masked = (q0 + TROWS > Lq) || (causal && qfirst < kmax_w) || ALIBI;
+      // Under the causal mask the ALiBi term of an item the key block sees
+      // in full is -slope * (q_pos - k_pos): its row part (with the LSE) is
+      // S's start value and its key part the per-lane offset; only ALiBi
+      // without the causal mask needs the per-element form everywhere.
+      const bool masked = (q0 + TROWS > Lq) || (causal && qfirst < kmax_w) || (ALIBI && !causal);
       // Lane element e of a block: key `key`, query row 32*qb + 16*(e/8) + 8*hf + e%8.
       // Carried across the barrier in the same registers: dP = dO V^T of both
       // blocks (dK wave), or P^T packed to bf16 pairs (dV wave, in hold[qb][0..7]).
@@ -276,9 +289,17 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
           // issue among the first block's exponentials.
           auto s_and_p = [&](auto masked_tag) {
             constexpr bool MASKED = decltype(masked_tag)::value;
+            const float kc = sl2 * (float)(my_kpos - qfirst);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-              const ra_f32x16 S = row_product(Qs[buf], qb);
+              ra_f32x16 S0 = ra_f32x16{};
+              if constexpr (ALIBI && !MASKED) {
+                const float4* lv4 = reinterpret_cast<const float4*>(&lsec_s[buf][32 * qb + 8 * hf]);
+                const float4 x0 = lv4[0], x1 = lv4[1], x2 = lv4[4], x3 = lv4[5];
+                S0 = ra_f32x16{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                               x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+              }
+              const ra_f32x16 S = row_product(Qs[buf], qb, S0);
               float p[16];
 #pragma unroll
               for (int e8 = 0; e8 < 2; ++e8) {
@@ -297,6 +318,9 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
                     const bool vis = (q0 + r0 + i < Lq) && key_ok && (!causal || my_kpos <= qv[i]);
                     p[8 * e8 + i] = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
                   }
+                } else if constexpr (ALIBI) {
+#pragma unroll
+                  for (int i = 0; i < 8; ++i) p[8 * e8 + i] = __builtin_amdgcn_exp2f(fmaf(S[8 * e8 + i], c, kc));
                 } else {
 #pragma unroll
                   for (int i = 0; i < 8; ++i) p[8 * e8 + i] = __builtin_amdgcn_exp2f(fmaf(S[8 * e8 + i], c, -lv[i]));
@@ -313,7 +337,7 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
           else s_and_p(std::false_type{});
         } else {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) hold[qb] = row_product(Os[buf], qb);
+          for (int qb = 0; qb < 2; ++qb) hold[qb] = row_product(Os[buf], qb, ra_f32x16{});
         }
       }
       if (!dv_wave && have_next) load_item(buf ^ 1, it + 1);
@@ -387,6 +411,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   __shared__ uint4 Ks[2][SLOTS];
   __shared__ uint4 Vs[2][SLOTS];
   __shared__ __align__(16) int kp[2][TROWS];
+  // Under ALiBi: slope * (k_pos - first key of the tile) / scale per key, the
+  // start value of S on the tiles the wave sees in full.
+  __shared__ __align__(16) float kbc[ALIBI ? 2 : 1][TROWS];
 
   const int Lq = a.len_q, Lkv = a.len_kv;
   // Query tiles in order of decreasing work across all heads (the last tile
@@ -425,6 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   const float my_lse2 = row_ok ? safe_lse2(a.lse[qhead * Lq + row]) : INFINITY;
   const float my_del = row_ok ? a.delta[qhead * Lq + row] : 0.0f;
   const float sl2 = ALIBI ? a.slopes[h] * RA_LOG2E : 0.0f;
+  const float sl2c = ALIBI ? a.slopes[h] / a.scale : 0.0f;
 
   // Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T.
   uint4 qf[KK], of[KK];
@@ -441,9 +469,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   const TileCopy<4> tc(wave, lane);
   auto load_kp = [&](int kv0) { return tid < TROWS ? kpos[min(kv0 + tid, Lkv - 1)] : 0; };
 
+  auto store_kp = [&](int buf, int kv0, int kpv) {
+    if (tid < TROWS) {
+      kp[buf][tid] = kpv;
+      if constexpr (ALIBI) kbc[buf][tid] = sl2c * (float)(kpv - kpos[kv0]);
+    }
+  };
   tc.copy(Ks[0], kh, 0, Lkv, wave, lane);
   tc.copy(Vs[0], vh, 0, Lkv, wave, lane);
-  if (tid < TROWS) kp[0][tid] = load_kp(0);
+  store_kp(0, 0, load_kp(0));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -463,10 +497,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
     const int klast = uniform_i(kp[buf][TROWS - 1]);
     if (wave_active && !(causal && kfirst > qmax_w)) {
       touched = true;
-      const bool diag = (kv0 + TROWS > Lkv) || (causal && klast > qmin_w) || ALIBI;
+      // Per-element masks only across the diagonal, on a ragged tile, or
+      // for ALiBi without the causal mask. Under the causal mask the ALiBi
+      // term of a tile the wave sees in full is -slope * (q_pos - k_pos): its
+      // key part is S's start value and its row part joins the LSE offset.
+      const bool diag = (kv0 + TROWS > Lkv) || (causal && klast > qmin_w) || (ALIBI && !causal);
+      const float row_off = ALIBI ? -my_lse2 - sl2 * (float)(my_pos - kfirst) : -my_lse2;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         ra_f32x16 S = ra_f32x16{}, dP = ra_f32x16{};
+        if constexpr (ALIBI) {
+          if (!diag) {
+            const float4* kv = reinterpret_cast<const float4*>(&kbc[buf][32 * sb + 8 * hf]);
+            const float4 x0 = kv[0], x1 = kv[1], x2 = kv[4], x3 = kv[5];
+            S = ra_f32x16{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                          x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+          }
+        }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           S = ra_mfma32(tile_row_frag(Ks[buf], 32 * sb, kk, lane), qf[kk], S);
@@ -493,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
           } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(S[8 * e8 + i], c, -my_lse2));
+              const float p = __builtin_amdgcn_exp2f(fmaf(S[8 * e8 + i], c, row_off));
               ds[i] = p * (dP[8 * e8 + i] - my_del);
             }
           }
@@ -510,7 +557,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
       }
     }
     if (!have_next) break;
-    if (tid < TROWS) kp[buf ^ 1][tid] = kp_next;
+    store_kp(buf ^ 1, kv0 + TROWS, kp_next);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (causal && uniform_i(kp[buf ^ 1][0]) > qmax_wg) break;  // keys past the last query
