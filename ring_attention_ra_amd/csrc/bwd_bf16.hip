@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
   __shared__ uint4 Qs[2][SLOTS];
   __shared__ uint4 Os[2][SLOTS];  // dO
   __shared__ __align__(16) float lse_s[2][TROWS];
-  __shared__ __align__(16) float del_s[2][TROWS];
+  __shared__ __align__(16) float del_s[2][TROWS];  // -delta per query row
   __shared__ __align__(16) int qp_s[2][TROWS];
   // Under ALiBi: -(lse * log2 e + slope * log2 e * (q_pos - first query of
   // the item)) / (scale * log2 e) per query row, the start value of S on the
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
       if (tid < TROWS) {
         const float l2 = safe_lse2(r.lse);
         lse_s[buf][tid] = l2;
-        del_s[buf][tid] = r.del;
+        del_s[buf][tid] = -r.del;  // the start value of dP
         qp_s[buf][tid] = r.qp;
         if constexpr (ALIBI) lsec_s[buf][tid] = -(l2 + r.sl2 * (float)(r.qp - r.qb)) / c;
       }
@@ -337,7 +337,15 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
           else s_and_p(std::false_type{});
         } else {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) hold[qb] = row_product(Os[buf], qb, ra_f32x16{});
+          for (int qb = 0; qb < 2; ++qb) {
+            // dP starts from -delta of its query rows, so that dP - delta
+            // comes out of the product.
+            const float4* d4 = reinterpret_cast<const float4*>(&del_s[buf][32 * qb + 8 * hf]);
+            const float4 x0 = d4[0], x1 = d4[1], x2 = d4[4], x3 = d4[5];
+            const ra_f32x16 nd = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                  x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+            hold[qb] = row_product(Os[buf], qb, nd);
+          }
         }
       }
       if (!dv_wave && have_next) load_item(buf ^ 1, it + 1);
@@ -359,16 +367,12 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
           for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
             for (int e8 = 0; e8 < 2; ++e8) {
-              const int r0 = 32 * qb + 16 * e8 + 8 * hf;
-              const float4 d0 = *reinterpret_cast<const float4*>(&del_s[buf][r0]);
-              const float4 d1 = *reinterpret_cast<const float4*>(&del_s[buf][r0 + 4]);
               const float4 pa = Px[kb][qb][2 * e8][lane], pb = Px[kb][qb][2 * e8 + 1][lane];
-              const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
               const float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
               for (int i = 0; i < 8; i += 2)
-                W[qb][4 * e8 + i / 2] = ra_pack_bf16(p[i] * (hold[qb][8 * e8 + i] - dv[i]),
-                                                     p[i + 1] * (hold[qb][8 * e8 + i + 1] - dv[i + 1]));
+                W[qb][4 * e8 + i / 2] = ra_pack_bf16(p[i] * hold[qb][8 * e8 + i],
+                                                     p[i + 1] * hold[qb][8 * e8 + i + 1]);
             }
           }
         }
