@@ -16,12 +16,19 @@ stream before the first step instead.
 
 Prints one JSON line. `value` is causal-effective TFLOP/s of the whole step
 (forward 4*D FLOP per visible (query, key) pair per query head, backward
-10*D). `roofline` is the dominant kernel (the bf16 step kernel) timed live
-with HIP events on the stream it runs on. `cpu_baseline` is the fp64 oracle
-timed on a bounded sample of the same workload on the host cores.
-`breakdown` adds the layout permutation's rate, the backward at 8*D per pair
-(without the recomputed S) next to the 10*D figure, and the rotary position
-embedding of the rank's K chunks, timed after the step as a separate pass.
+10*D), from the mean step time of the timed region; `breakdown` also gives
+the median of the per-step times (HIP events on the launch stream).
+`roofline` is the dominant kernel timed live with HIP events on the stream it
+runs on: the forward step kernel (ra_step_fwd), or for the workloads with a
+backward the backward step (ra_step_bwd, its two kernels), whose time
+dominates there. It also carries the step's algorithmic HBM bytes per launch
+and the rate they imply. `cpu_baseline` is the fp64 oracle timed on a bounded
+sample of the same workload on the host cores. `breakdown` adds the layout
+permutation's rate, the backward at 8*D per pair (without the recomputed S)
+next to the 10*D figure, the shader clock read from the device over untimed
+steps run after the timed region (with the peak scaled to it), and the rotary
+position embedding
+of the rank's K chunks, timed after the step as a separate pass.
 """
 
 from __future__ import annotations
@@ -30,6 +37,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -45,6 +53,72 @@ from ring_attention_ra_amd import _lib, configs, ring  # noqa: E402
 PEAK_HBM_TBS = 8.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0  # the clock the bf16 peak is quoted at
+
+
+class ClockReader:
+    """Reads the GPU's shader clock (MHz, mean over the XCDs) from the
+    device's metrics table through amdsmi; None when amdsmi is missing or
+    refuses."""
+
+    def __init__(self):
+        self._api = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if len(handles) == 1 or (bus is not None and int(bdf.split(":")[1], 16) == int(bus)):
+                    self._handle = h
+                    self._api = amdsmi
+        except Exception:  # noqa: BLE001 - the clock is optional
+            self._api = None
+
+    def read(self):
+        if self._api is None:
+            return None
+        try:
+            m = self._api.amdsmi_get_gpu_metrics_info(self._handle)
+        except Exception:  # noqa: BLE001
+            return None
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 10000]
+        if clks:
+            return sum(clks) / len(clks)
+        c = m.get("current_gfxclk")
+        return float(c) if isinstance(c, int) and 0 < c < 10000 else None
+
+
+def clock_window(step, reader, seconds, ms_per_step):
+    """The shader clock under the same load: after the timed region, run
+    untimed steps for about `seconds`, keeping two steps in flight, and read
+    the clock after each (the metrics table refreshes a few times per second,
+    so one sample is kept per distinct reading)."""
+    if reader.read() is None:
+        return None
+    n = max(20, int(seconds * 1e3 / max(ms_per_step, 1e-3)))
+    done = []
+    samples = []
+    for i in range(n):
+        step(False)
+        ev = torch.cuda.Event()
+        ev.record()
+        done.append(ev)
+        if i >= 2:
+            done[i - 2].synchronize()
+            v = reader.read()
+            if v is not None:
+                samples.append(v)
+    torch.cuda.synchronize()
+    if not samples:
+        return None
+    body = samples[len(samples) // 5:]  # the first reads may predate the load
+    distinct = [v for k, v in enumerate(body) if k == 0 or v != body[k - 1]]
+    return {"gfx_mhz_mean": round(statistics.fmean(distinct), 1), "gfx_mhz_min": round(min(distinct), 1),
+            "gfx_mhz_max": round(max(distinct), 1), "readings": len(distinct), "window_steps": n,
+            "source": "amdsmi gpu metrics (current_gfxclks), untimed steps after the timed region"}
 
 
 def visible_pairs_per_chunk(w, pos_cpu):
@@ -68,13 +142,14 @@ def parse():
     ap.add_argument("--workload", default=str(configs.HEADLINE.index),
                     help="workload index (1-6) or name; default: the 128K zig-zag share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the clock reading window after the timed region")
     ap.add_argument("--serial-permute", action="store_true",
                     help="permute every K/V chunk on the launch stream before the first step")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows in the CPU-baseline sample")
     ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-baseline sample")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fwd_bf16_128k_zigzag_traffic.json"),
-                    help="JSON with counter-measured HBM bytes per step-kernel launch; used only when it was "
-                         "taken on this workload and on the current kernel source")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "step_kernel_traffic.json"),
+                    help="JSON records of counter-measured HBM bytes per launch of a step kernel; a record is "
+                         "used only when it was taken on this workload and on the current kernel source")
     return ap.parse_args()
 
 
@@ -153,7 +228,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     side = torch.cuda.Stream(device=dev)  # default priority
-    fwd_events, bwd_events, perm_events, side_events = [], [], [], []
+    fwd_events, bwd_events, perm_events, side_events, step_events = [], [], [], [], []
 
     def ev(on=None):
         e = torch.cuda.Event(enable_timing=True)
@@ -163,6 +238,7 @@ def main():
     def step(timed):
         ready = {}
         if timed:
+            step_events.append(ev())
             perm_events.append(ev())
         _lib.ra_layout_permute(q_g, q_loc, None, b * hq, s, d, n, w.layout, rank=w.rank)
         if args.serial_permute:
@@ -210,6 +286,8 @@ def main():
                                  slopes, d_o, lse, delta, dq, dk[src], dv[src])
                 if timed:
                     bwd_events.append(ev())
+        if timed:
+            step_events.append(ev())
 
     for _ in range(args.warmup):
         step(False)
@@ -220,6 +298,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    clk = None if args.no_clock else clock_window(step, ClockReader(), 1.5, ms_per_step)
 
     pairs = visible_pairs_per_chunk(w, pos.cpu())
     fwd_flops = 4.0 * d * hq * b * sum(pairs)
@@ -230,6 +309,8 @@ def main():
     def pair_ms(evs):
         return [evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2)]
 
+    step_ms = pair_ms(step_events)
+    median_ms = statistics.median(step_ms)
     fwd_ms = pair_ms(fwd_events)
     fwd_launch_ms = sum(fwd_ms) / len(fwd_ms)
     fwd_total_ms = sum(fwd_ms) / args.steps
@@ -243,26 +324,50 @@ def main():
         side_ms = sum(pair_ms(side_events)) / args.steps
         side_bytes = 2.0 * (n - 1) * (k_ch[0].numel() + v_ch[0].numel()) * esz + (n - 1) * pos[0].numel() * 4
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
+    # Algorithmic HBM bytes of one forward step through the step API: a step
+    # with a visible pair reads Q and the K/V chunk, and reads and writes the
+    # fp32 state (o_acc, m, l); a fully masked step moves nothing.
+    q_bytes = b * hq * c * d * esz
+    kv_bytes = 2 * b * hkv * c * d * esz
+    state_bytes = 2 * (b * hq * c * d * 4 + 2 * b * hq * c * 4)
+    fwd_alg_bytes = sum(q_bytes + kv_bytes + state_bytes for p_ in pairs if p_ > 0) / n
+
+    def traffic_for(kernel, source):
+        """Counter-measured bytes per launch, if a record matches the workload
+        and the kernel source as it is now."""
+        if not (args.traffic and os.path.exists(args.traffic)):
+            return None
         with open(args.traffic) as f:
-            rec = json.load(f)
-        src = os.path.join(ROOT, "ring_attention_ra_amd", "csrc", "fwd_bf16.hip")
-        with open(src, "rb") as f:
+            recs = json.load(f).get("records", [])
+        with open(os.path.join(ROOT, "ring_attention_ra_amd", "csrc", source), "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
-        if rec.get("kernel_source_sha256") == sha and rec.get("workload") == w.name:
-            traffic = rec.get("bytes_per_launch")
+        for rec in recs:
+            if rec.get("kernel") == kernel and rec.get("workload") == w.name and \
+                    rec.get("kernel_source_sha256") == sha:
+                return rec.get("bytes_per_launch")
+        return None
 
     extra = {
+        "median_ms_per_step": round(median_ms, 4),
+        "value_at_median": round(step_flops / (median_ms * 1e-3) / 1e12, 3),
         "step_kernel_tflops": round(fwd_tflops, 2),
         "step_kernel_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
         "step_kernel_ms_per_step": round(fwd_total_ms, 4),
+        "step_kernel_launch_ms": round(fwd_launch_ms, 4),
+        "step_kernel_alg_bytes_per_launch": int(fwd_alg_bytes),
+        "step_kernel_hbm_gbs": round(fwd_alg_bytes / (fwd_launch_ms * 1e-3) / 1e9, 1),
+        "step_kernel_frac_of_hbm": round(fwd_alg_bytes / (fwd_launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "permute_ms_per_step": round(perm_ms, 4),
         "permute_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
         "permute_scope": "every chunk, launch stream" if args.serial_permute else "own Q/K/V chunks, launch stream",
         "visible_pairs_per_head": sum(pairs),
         "fwd_flop_per_step": fwd_flops,
     }
+    if clk:
+        peak_clk = PEAK_BF16_TFLOPS * clk["gfx_mhz_mean"] / PEAK_CLOCK_MHZ
+        clk["bf16_peak_at_clock_tflops"] = round(peak_clk, 1)
+        clk["value_frac_of_peak_at_clock"] = round(value / peak_clk, 4)
+    extra["clock"] = clk
     if not args.serial_permute:
         # The other ranks' chunks on the side stream, one per step, each
         # overlapped with a step (so not a rate of its own).
@@ -289,14 +394,42 @@ def main():
     extra["rope"] = {"kernel": "rope_kernel (ra_rope)", "tensor": "K chunks [N,B,Hkv,C,D]", "ms": round(rope_ms, 4),
                      "gbs": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
                      "frac_of_hbm": round(rope_bytes / (rope_ms * 1e-3) / 1e12 / PEAK_HBM_TBS, 4)}
+
+    roofline = {
+        "bound": "mfma",
+        "achieved": round((fwd_flops / n) / (fwd_launch_ms * 1e-3) / 1e12, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": None,
+        "traffic": traffic_for("fwd_bf16_kernel", "fwd_bf16.hip"),
+        "kernel": "fwd_bf16_kernel (ra_step_fwd)",
+        "launch_ms": round(fwd_launch_ms, 4),
+        "flop_per_launch": fwd_flops / n,
+        "alg_bytes_per_launch": int(fwd_alg_bytes),
+    }
     if w.backward:
         bwd_ms = pair_ms(bwd_events)
         bwd_total_ms = sum(bwd_ms) / args.steps
+        bwd_launch_ms = sum(bwd_ms) / len(bwd_ms)
         extra["bwd_kernel_ms_per_step"] = round(bwd_total_ms, 4)
         extra["bwd_kernel_tflops"] = round(bwd_flops / (bwd_total_ms * 1e-3) / 1e12, 2)
         # The same time counted without the recomputed S (8*D per visible pair).
         extra["bwd_kernel_tflops_8d"] = round(0.8 * bwd_flops / (bwd_total_ms * 1e-3) / 1e12, 2)
         extra["bwd_flop_per_step"] = bwd_flops
+        extra["fwd_roofline"] = dict(roofline, frac=round(roofline["achieved"] / PEAK_BF16_TFLOPS, 4))
+        # The backward step dominates the time here: it is the roofline kernel.
+        roofline = {
+            "bound": "mfma",
+            "achieved": round((bwd_flops / n) / (bwd_launch_ms * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": None,
+            "traffic": traffic_for("bwd_step (bwd_dkdv_kernel + bwd_dq_kernel)", "bwd_bf16.hip"),
+            "kernel": "bwd_dkdv_kernel + bwd_dq_kernel (ra_step_bwd)",
+            "launch_ms": round(bwd_launch_ms, 4),
+            "flop_per_launch": bwd_flops / n,
+        }
+    roofline["frac"] = round(roofline["achieved"] / PEAK_BF16_TFLOPS, 4)
 
     result = {
         "metric": "causal attention TFLOP/s per ring-rank share + % of bf16 MFMA peak",
@@ -313,20 +446,9 @@ def main():
         "data": "synthetic (seeded N(0, std^2) inputs, see seeded_inputs.py)",
         "config": w.describe(),
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round((fwd_flops / n) / (fwd_launch_ms * 1e-3) / 1e12, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": None,
-            "traffic": traffic,
-            "kernel": "fwd_bf16_kernel (ra_step_fwd)",
-            "launch_ms": round(fwd_launch_ms, 4),
-            "flop_per_launch": fwd_flops / n,
-        },
+        "roofline": roofline,
         "breakdown": extra,
     }
-    result["roofline"]["frac"] = round(result["roofline"]["achieved"] / PEAK_BF16_TFLOPS, 4)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, q_g, k_g, v_g, args.cpu_rows, args.cpu_heads)
         cb["value"] = round(cb["value"], 5)

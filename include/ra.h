@@ -18,9 +18,11 @@
  *
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
- *    The library allocates no device memory and keeps no mutable global state
- *    besides the thread-local error text; calls from several host threads are
- *    safe.
+ *    The compute entry points allocate no device memory and keep no mutable
+ *    global state besides the thread-local error text; calls from several
+ *    host threads are safe. Only the optional checks below (and
+ *    ra_count_nonfinite) hold a small device counter array for the length of
+ *    the call.
  *  - Tensors are dense and row-major in the order written: [B, H, L, D] has D
  *    fastest. Positions are int32 and shared by all batches and heads.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
@@ -29,6 +31,20 @@
  *    error nothing is launched and ra_last_error() describes the problem.
  *  - A dimension of zero (empty batch, heads or lengths) is valid and
  *    enqueues nothing.
+ *  - Optional checks, switched on per process by environment variables read
+ *    at every call (unset or "0" = off). Both make the call wait for its
+ *    stream.
+ *      RA_CHECK_FINITE=1: ra_step_fwd, ra_finalize, ra_bwd_delta, ra_step_bwd
+ *        and ra_rope check that their tensor inputs are finite before
+ *        enqueuing any work (a corrupted chunk then leaves the state
+ *        untouched) and that their outputs are finite afterwards (m and lse
+ *        may be -Inf, l must not be negative), returning RA_ERR_NONFINITE
+ *        with the tensor named in ra_last_error(). A ring hands every chunk
+ *        from device to device, and a corrupted transfer shows up as NaN or
+ *        Inf in what a rank receives (discosf.com article, §5.2 典型问题排查).
+ *      RA_DEBUG=1: ra_step_fwd and ra_step_bwd check the precondition that
+ *        q_pos and k_pos are non-negative and strictly increasing, returning
+ *        RA_ERR_INVALID_ARGUMENT before any launch if they are not.
  */
 #ifndef RA_H
 #define RA_H
@@ -43,7 +59,8 @@ typedef enum ra_status {
   RA_OK = 0,
   RA_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, negative size, bad enum, inconsistent shape */
   RA_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement (e.g. head_dim) */
-  RA_ERR_HIP = 3               /* the HIP runtime reported an error on launch */
+  RA_ERR_HIP = 3,              /* the HIP runtime reported an error on launch */
+  RA_ERR_NONFINITE = 4         /* a checked tensor holds NaN or Inf (RA_CHECK_FINITE=1) */
 } ra_status;
 
 typedef enum ra_dtype { RA_BF16 = 0, RA_FP32 = 1 } ra_dtype;
@@ -133,6 +150,11 @@ ra_status ra_state_init(const ra_dims* d, float* o_acc, float* m, float* l, void
  * that); tiles that are masked out entirely are skipped using this.
  * Positions must be non-negative. For bf16, q, k_blk, v_blk and o_acc must be
  * 16-byte aligned (RA_ERR_INVALID_ARGUMENT otherwise).
+ * Size limits (RA_ERR_UNSUPPORTED beyond them, checked before any launch):
+ * bf16 addresses one head's o_acc slab through a 32-bit buffer resource, so
+ * len_q * head_dim * 4 must stay below 2^31 (len_q <= 4,194,303 at
+ * head_dim 128); the number of work-groups (one per 128 rows of a head, bf16,
+ * or 32 rows, fp32, at most) must fit in int32.
  * Computation: bf16 inputs use bf16 MFMA with fp32 accumulation (P is rounded
  * to bf16 before the P.V product); fp32 inputs are computed in fp32. */
 ra_status ra_step_fwd(const ra_dims* d, const void* q, const void* k_blk, const void* v_blk,
@@ -161,12 +183,27 @@ ra_status ra_bwd_delta(const ra_dims* d, const void* o, const void* d_o, float* 
  * Same masking, positions and ALiBi term as ra_step_fwd. dq_acc
  * [B,Hq,Lq,D], dk_blk and dv_blk [B,Hkv,Lkv,D] are fp32 and ACCUMULATE
  * (caller zeroes them once); query heads sharing a K/V head add into it.
- * Supported for RA_BF16 with head_dim 128; deterministic (no atomics). */
+ * Supported for RA_BF16 with head_dim 128 (bf16 matrix-core products with
+ * fp32 accumulation; P and dS are rounded to bf16 before their products) and
+ * for RA_FP32 with head_dim 1..128 (computed in fp32 throughout: the
+ * correctness path). Deterministic (no atomics).
+ * Size limits (RA_ERR_UNSUPPORTED beyond them): for bf16 one head's q / d_o
+ * slab and k / v slab must stay below 2^31 bytes (len_q, len_kv <= 8,388,607
+ * at head_dim 128); the work-group count must fit in int32. */
 ra_status ra_step_bwd(const ra_dims* d, const void* q, const void* k_blk, const void* v_blk,
                       const int32_t* q_pos, const int32_t* k_pos, int32_t causal, float scale,
                       const float* alibi_slopes, const void* d_o, const float* lse,
                       const float* delta, float* dq_acc, float* dk_blk, float* dv_blk,
                       void* stream);
+
+/* Number of NaN or Inf elements among the n elements of x (a device tensor
+ * of `dtype`), counted on the GPU on `stream`; the call waits for the count
+ * and writes it to *count (host memory). Lets a caller check a chunk it has
+ * received before folding it in (discosf.com article, §5.2 典型问题排查: a
+ * ring transfer may corrupt data). Holds a small device counter array,
+ * allocated and freed inside the call. Errors: count NULL, n negative, x NULL
+ * with n > 0, unknown dtype. */
+ra_status ra_count_nonfinite(const void* x, int64_t n, int32_t dtype, int64_t* count, void* stream);
 
 /* Text for the last non-OK status returned on this host thread ("" if none). */
 const char* ra_last_error(void);

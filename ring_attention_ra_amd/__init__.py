@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     RaError,
     ra_abi_version,
     ra_bwd_delta,
+    ra_count_nonfinite,
     ra_finalize,
     ra_last_error,
     ra_layout_permute,

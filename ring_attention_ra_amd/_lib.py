@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("RA_LIB") or os.path.join(PKG, "libra.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "ra.h")
 
-RA_OK, RA_ERR_INVALID_ARGUMENT, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
+RA_OK, RA_ERR_INVALID_ARGUMENT, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_NONFINITE = 0, 1, 2, 3, 4
 RA_BF16, RA_FP32 = 0, 1
 RA_CONTIGUOUS, RA_ZIGZAG = 0, 1
 
@@ -56,6 +56,7 @@ _SIGNATURES = {
     "ra_finalize": [_DIMS, _P, _P, _P, _P, _P, _P],
     "ra_bwd_delta": [_DIMS, _P, _P, _P, _P],
     "ra_step_bwd": [_DIMS, _P, _P, _P, _P, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
+    "ra_count_nonfinite": [_P, _I64, _I32, ctypes.POINTER(ctypes.c_int64), _P],
     "ra_last_error": [],
     "ra_abi_version": [],
 }
@@ -219,6 +220,15 @@ def ra_step_bwd(dims, q, k_blk, v_blk, q_pos, k_pos, causal, scale, alibi_slopes
         _ptr(delta, "delta", torch.float32, rows), _ptr(dq_acc, "dq_acc", torch.float32, rows * dims.head_dim),
         _ptr(dk_blk, "dk_blk", torch.float32, kv), _ptr(dv_blk, "dv_blk", torch.float32, kv),
         _stream(stream)), "ra_step_bwd")
+
+
+def ra_count_nonfinite(x, stream=None) -> int:
+    """Number of NaN / Inf elements of the bf16 or fp32 GPU tensor x (waits
+    for the stream)."""
+    n = ctypes.c_int64(-1)
+    _check(lib().ra_count_nonfinite(_ptr(x, "x"), x.numel(), dtype_code(x.dtype), ctypes.byref(n),
+                                    _stream(stream)), "ra_count_nonfinite")
+    return int(n.value)
 
 
 def ra_last_error() -> str:

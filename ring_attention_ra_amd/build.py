@@ -23,7 +23,7 @@ ARCH = "gfx950"
 # Packed fp32 VALU instructions are kept out of generated code on purpose.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+             "-Wall", "-Wno-unused-function", "-Werror=inline-asm", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def hipcc() -> str:

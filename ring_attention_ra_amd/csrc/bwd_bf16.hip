@@ -43,7 +43,7 @@ constexpr int D = 128;
 constexpr int CPR = 16;             // 16-byte chunks per row
 constexpr int KK = D / 16;          // k-steps over d
 constexpr int DT = D / 32;          // 32-wide d tiles
-constexpr int TROWS = 64;           // rows per streamed tile
+constexpr int TROWS = kTileRows;    // rows per streamed tile (64)
 constexpr int SLOTS = TROWS * CPR;  // 16-byte slots per tile
 
 __device__ __forceinline__ float safe_lse2(float lse) {
@@ -52,7 +52,7 @@ __device__ __forceinline__ float safe_lse2(float lse) {
 }
 
 // A 64-row tile is copied by NW waves, DPW = SLOTS / (64 * NW) 16-byte slots
-// per lane; slot p holds row p / 16, physical chunk p % 16 (tile_swz layout).
+// per lane, in the layout of tile_slot.
 template <int NW>
 struct TileCopy {
   static constexpr int DPW = SLOTS / (64 * NW);
@@ -60,9 +60,9 @@ struct TileCopy {
   __device__ __forceinline__ TileCopy(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
-      const int p = (wave * DPW + i) * 64 + lane;
-      const int r = p / CPR, ph = p % CPR;
-      off[i] = (uint32_t)(r * D + 8 * (ph ^ tile_swz(r))) * 2;
+      int r;
+      const int ch = tile_slot_chunk((wave * DPW + i) * 64 + lane, &r);
+      off[i] = (uint32_t)(r * D + 8 * ch) * 2;
     }
   }
   // Copy rows [row0, row0 + 64) of a [L, 128] bf16 matrix (0 <= row0 < L);
@@ -77,8 +77,10 @@ struct TileCopy {
       const int last = L - 1 - row0;
 #pragma unroll
       for (int i = 0; i < DPW; ++i) {
-        const int bs = (wave * DPW + i) * 64, p = bs + lane, r = p / CPR, ph = p % CPR;
-        dma16(t + (uint32_t)(min(r, last) * D + 8 * (ph ^ tile_swz(r))) * 2, &tile[bs]);
+        const int bs = (wave * DPW + i) * 64;
+        int r;
+        const int ch = tile_slot_chunk(bs + lane, &r);
+        dma16(t + (uint32_t)(min(r, last) * D + 8 * ch) * 2, &tile[bs]);
       }
     }
   }
@@ -125,6 +127,9 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
   const bool wave_active = kw0 < Lkv;
   const bool causal = a.causal != 0;
   const float c = a.scale * RA_LOG2E;
+  // The linear form of the ALiBi term divides by c: with c <= 0 every item
+  // takes the per-element path (as in the forward step).
+  const bool lin_ok = c > 0.0f;
 
   const int64_t khead = (int64_t)b * a.heads_kv + hk;
   // K fragments (B operand of S = Q K^T) for the dV wave, V fragments (B
@@ -191,39 +196,15 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
         lse_s[buf][tid] = l2;
         del_s[buf][tid] = -r.del;  // the start value of dP
         qp_s[buf][tid] = r.qp;
-        if constexpr (ALIBI) lsec_s[buf][tid] = -(l2 + r.sl2 * (float)(r.qp - r.qb)) / c;
+        if constexpr (ALIBI) lsec_s[buf][tid] = lin_ok ? -(l2 + r.sl2 * (float)(r.qp - r.qb)) / c : 0.0f;
       }
     };
 
-    // Per-lane parts of the fragment addresses. A row fragment of rows
-    // r0 + perm_row(lane%32), k-step kk sits at byte r0*256 + (kk/4)*128 +
-    // rofs[kk%4]; a column fragment (tile_col_frag) of rows r0, columns 32*dt
-    // at r0*256 + (dt/2)*128 + cofs[half][dt%2] (the swizzle of a row depends
-    // only on its offset inside a 16-row group, so r0 and the high column bit
-    // add as constants).
-    int rofs[4], cofs[2][2];
-    {
-      const int pr = perm_row(l32), gq = (lane >> 4) & 1, j = lane & 15;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) rofs[m] = pr * 256 + ((2 * m + hf) ^ tile_swz(pr)) * 16;
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const int rl = 8 * hf + 4 * half + (j >> 2), x = 2 * gq + ((j & 3) >> 1);
-          cofs[half][db] = rl * 256 + ((4 * db + x) ^ tile_swz(rl)) * 16 + 8 * (j & 1);
-        }
-    }
-    auto row_frag = [&](const uint4* tile, int r0, int kk) {
-      return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + r0 * 256 + (kk >> 2) * 128 +
-                                             rofs[kk & 3]);
-    };
-    auto col_frag = [&](const uint4* tile, int r0, int dt) {
-      const char* t = reinterpret_cast<const char*>(tile) + r0 * 256 + (dt >> 1) * 128;
-      const uint2 a0 = lds_tr4(t + cofs[0][dt & 1]);
-      const uint2 a1 = lds_tr4(t + cofs[1][dt & 1]);
-      return make_uint4(a0.x, a0.y, a1.x, a1.y);
-    };
+    // Per-lane parts of the fragment addresses (the rest folds into the
+    // instructions' immediate offsets).
+    const FragOffsets fo(lane);
+    auto row_frag = [&](const uint4* tile, int r0, int kk) { return tile_row_frag(tile, r0, kk, fo); };
+    auto col_frag = [&](const uint4* tile, int r0, int dt) { return tile_col_frag(tile, r0, dt, fo); };
     // One 32-query block's product A(rows) x bf^T: S (dV wave) or dP (dK wave).
     constexpr int LA = 3;
     auto row_product = [&](const uint4* tile, int qb, ra_f32x16 r) {
@@ -272,7 +253,7 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
       // in full is -slope * (q_pos - k_pos): its row part (with the LSE) is
       // S's start value and its key part the per-lane offset; only ALiBi
       // without the causal mask needs the per-element form everywhere.
-      const bool masked = (q0 + TROWS > Lq) || (causal && qfirst < kmax_w) || (ALIBI && !causal);
+      const bool masked = (q0 + TROWS > Lq) || (causal && qfirst < kmax_w) || (ALIBI && !(causal && lin_ok));
       // Lane element e of a block: key `key`, query row 32*qb + 16*(e/8) + 8*hf + e%8.
       // Carried across the barrier in the same registers: dP = dO V^T of both
       // blocks (dK wave), or P^T packed to bf16 pairs (dV wave, in hold[qb][0..7]).
@@ -455,8 +436,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   const int my_pos = row_ok ? a.q_pos[row] : INT32_MAX;
   const float my_lse2 = row_ok ? safe_lse2(a.lse[qhead * Lq + row]) : INFINITY;
   const float my_del = row_ok ? a.delta[qhead * Lq + row] : 0.0f;
+  // The linear form of the ALiBi term divides by the scale: with c <= 0
+  // every tile takes the per-element path (as in the forward step).
+  const bool lin_ok = c > 0.0f;
   const float sl2 = ALIBI ? a.slopes[h] * RA_LOG2E : 0.0f;
-  const float sl2c = ALIBI ? a.slopes[h] / a.scale : 0.0f;
+  const float sl2c = (ALIBI && lin_ok) ? a.slopes[h] / a.scale : 0.0f;
 
   // Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T.
   uint4 qf[KK], of[KK];
@@ -471,6 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   bool touched = false;
 
   const TileCopy<4> tc(wave, lane);
+  const FragOffsets fo(lane);
   auto load_kp = [&](int kv0) { return tid < TROWS ? kpos[min(kv0 + tid, Lkv - 1)] : 0; };
 
   auto store_kp = [&](int buf, int kv0, int kpv) {
@@ -505,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
       // for ALiBi without the causal mask. Under the causal mask the ALiBi
       // term of a tile the wave sees in full is -slope * (q_pos - k_pos): its
       // key part is S's start value and its row part joins the LSE offset.
-      const bool diag = (kv0 + TROWS > Lkv) || (causal && klast > qmin_w) || (ALIBI && !causal);
+      const bool diag = (kv0 + TROWS > Lkv) || (causal && klast > qmin_w) || (ALIBI && !(causal && lin_ok));
       const float row_off = ALIBI ? -my_lse2 - sl2 * (float)(my_pos - kfirst) : -my_lse2;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
@@ -520,8 +505,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
         }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          S = ra_mfma32(tile_row_frag(Ks[buf], 32 * sb, kk, lane), qf[kk], S);
-          dP = ra_mfma32(tile_row_frag(Vs[buf], 32 * sb, kk, lane), of[kk], dP);
+          S = ra_mfma32(tile_row_frag(Ks[buf], 32 * sb, kk, fo), qf[kk], S);
+          dP = ra_mfma32(tile_row_frag(Vs[buf], 32 * sb, kk, fo), of[kk], dP);
         }
         // Lane element e: query `row`, key 32*sb + 16*(e/8) + 8*hf + e%8.
         uint32_t Dw[8];
@@ -556,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
           const uint4 db = make_uint4(Dw[4 * ks], Dw[4 * ks + 1], Dw[4 * ks + 2], Dw[4 * ks + 3]);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-            dQ[dt] = ra_mfma32(tile_col_frag(Ks[buf], 32 * sb + 16 * ks, 32 * dt, lane), db, dQ[dt]);
+            dQ[dt] = ra_mfma32(tile_col_frag(Ks[buf], 32 * sb + 16 * ks, dt, fo), db, dQ[dt]);
         }
       }
     }

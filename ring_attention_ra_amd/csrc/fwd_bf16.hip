@@ -74,8 +74,10 @@
 //    per-row constant.
 //  * Work-groups are ordered heaviest-first and, when the counts allow, each
 //    XCD is given whole heads so that its L2 serves one head's K/V stream.
-//  * LDS rows are XOR-swizzled in 16-byte units so that the fragment reads of
-//    a wave spread over the banks.
+//  * K and V tiles are stored as 64-column halves with XOR-swizzled 16-byte
+//    chunks, so that neither the K row reads nor the transposing V reads meet
+//    a bank conflict and the fragment addresses keep folding into immediate
+//    offsets.
 #include <type_traits>
 
 #include "tile_common.h"
@@ -84,7 +86,7 @@ namespace ra {
 namespace {
 
 constexpr int BM = 256;  // query rows per work-group (two sets of 4 waves x 32 rows)
-constexpr int BN = 64;   // keys per tile
+constexpr int BN = kTileRows;  // keys per tile (64)
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 units
@@ -96,12 +98,8 @@ enum TileMode { kFast = 0, kAlibiLinear = 1, kExact = 2 };
 // like dma16: untracked by the compiler, awaited explicitly).
 __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
   const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ra_lds_void*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(la) : "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(la));
 }
-
-// 16-byte chunk swizzles of the K and V rows in LDS.
-__device__ __forceinline__ int k_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
 
 // Scheduling pattern of one MFMA phase: NQK QK products (one LDS read each)
 // followed by NPV P.V products (two transposing LDS reads each). The reads of
@@ -232,13 +230,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   // ---- tile movement ----
   // Phase-1 copies: every wave moves DMA_PER_WAVE 16-byte slots of a K
   // tile and of a V tile (offsets precomputed).
-  uint32_t dk_off[DMA_PER_WAVE], dv_off[DMA_PER_WAVE];
+  // K and V tiles share the layout of tile_slot, so one set of source
+  // offsets serves both.
+  uint32_t d_off[DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int p = (wave * DMA_PER_WAVE + i) * 64 + lane;
-    const int r = p / CPR, ph = p % CPR;
-    dk_off[i] = (uint32_t)(r * D + 8 * (ph ^ k_swz(r))) * 2;
-    dv_off[i] = (uint32_t)(r * D + 8 * (ph ^ v_swz(r))) * 2;
+    int r;
+    const int ch = tile_slot_chunk((wave * DMA_PER_WAVE + i) * 64 + lane, &r);
+    d_off[i] = (uint32_t)(r * D + 8 * ch) * 2;
   }
   auto dma_p1 = [&](int kbuf, int kv0k, int vbuf, int kv0v) {  // complete tiles only
     const char* kt = reinterpret_cast<const char*>(kh + (int64_t)kv0k * D);
@@ -246,26 +245,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       const int base = (wave * DMA_PER_WAVE + i) * 64;
-      dma16(kt + dk_off[i], &Ks[kbuf][base]);
-      dma16(vt + dv_off[i], &Vs[vbuf][base]);
+      dma16(kt + d_off[i], &Ks[kbuf][base]);
+      dma16(vt + d_off[i], &Vs[vbuf][base]);
     }
     // ALiBi: wave 0 also copies the key positions of the K tile.
     if constexpr (ALIBI) if (wave == 0) dma4(kpos + kv0k + lane, &kp[kbuf][0]);
   };
   // All eight waves; rows past the end of the chunk are clamped to the last
   // key (they are masked).
-  auto dma_all = [&](uint4* tile, const uint16_t* src, int kv0, bool is_v) {
+  auto dma_all = [&](uint4* tile, const uint16_t* src, int kv0) {
     const char* t = reinterpret_cast<const char*>(src + (int64_t)kv0 * D);
     const int last = Lkv - 1 - kv0;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int base = (wave * DMA_PER_WAVE + i) * 64, p = base + lane, r = p / CPR, ph = p % CPR;
-      const int sw = is_v ? v_swz(r) : k_swz(r);
-      dma16(t + (uint32_t)(min(r, last) * D + 8 * (ph ^ sw)) * 2, &tile[base]);
+      const int base = (wave * DMA_PER_WAVE + i) * 64;
+      int r;
+      const int ch = tile_slot_chunk(base + lane, &r);
+      dma16(t + (uint32_t)(min(r, last) * D + 8 * ch) * 2, &tile[base]);
     }
   };
-  auto dma_k = [&](int buf, int kv0) { dma_all(Ks[buf], kh, kv0, false); };
-  auto dma_v = [&](int buf, int kv0) { dma_all(Vs[buf], vh, kv0, true); };
+  auto dma_k = [&](int buf, int kv0) { dma_all(Ks[buf], kh, kv0); };
+  auto dma_v = [&](int buf, int kv0) { dma_all(Vs[buf], vh, kv0); };
   auto load_kp = [&](int kv0) { return tid < BN ? kpos[min(kv0 + tid, Lkv - 1)] : 0; };
   auto store_kp = [&](int buf, int kv0, int kpv) {
     if (tid < BN) {
@@ -333,19 +333,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   if (p1_possible) T1 = Lkv / BN;
   if (causal) tile_counts(kpos, T, qmax_wg, p1_possible ? T1 : 0, qmin_wg, lane, T, T1);
 
-  // V^T fragment for d tile dt and keys kb0 + 8*hf + 0..7 (two transposing reads).
-  const int g16 = lane >> 4, j16 = lane & 15;
-  auto v_frag = [&](int buf, int kb0, int dt) {
-    const int d0 = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
-    uint2 r2[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int r = kb0 + 8 * hf + 4 * half + (j16 >> 2);
-      const int ch = (d0 >> 3) ^ v_swz(r);
-      r2[half] = lds_tr4(reinterpret_cast<const char*>(&Vs[buf][r * CPR + ch]) + 2 * (d0 & 7));
-    }
-    return make_uint4(r2[0].x, r2[0].y, r2[1].x, r2[1].y);
-  };
+  // V^T fragment for d tile dt and keys kb0 + 8*hf + 0..7 (two transposing
+  // reads); K fragment of rows 32*sb + perm_row(lane%32), k-step kk.
+  const FragOffsets fo(lane);
+  auto v_frag = [&](int buf, int kb0, int dt) { return tile_col_frag(Vs[buf], kb0, dt, fo); };
 
   // Scores of the tile (two 32-key blocks, S[sb] element e = key 32*sb +
   // 16*(e/8) + 8*hf + e%8) and its bf16 probabilities P[sb][8] for the next
@@ -366,10 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
       }
     }
   };
-  auto k_frag = [&](int kbuf, int sb, int kk) {
-    const int krow = 32 * sb + perm_row(l32);
-    return Ks[kbuf][krow * CPR + ((2 * kk + hf) ^ k_swz(krow))];
-  };
+  auto k_frag = [&](int kbuf, int sb, int kk) { return tile_row_frag(Ks[kbuf], 32 * sb, kk, fo); };
   auto qk_mfma = [&](int kbuf) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -690,6 +678,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     }
   }
 
+  // When the ping-pong loop took every tile its last copies may still be in
+  // flight: let them land before the work-group can end and free its LDS.
+  __builtin_amdgcn_s_waitcnt(0);
   if (!touched) return;
   // Write the state back, taken against the reference.
   const float l_tot = l_run + ra_swap_halves(l_run);

@@ -66,6 +66,28 @@ struct BwdArgs {
   float scale;
 };
 
+// One tensor (or position list) for the optional device-side checks.
+enum CheckKind {
+  kCheckFinite = 0,         // every element finite
+  kCheckNoNanNoPosInf = 1,  // no NaN and no +Inf (-Inf allowed: m and lse of rows with no key)
+  kCheckFiniteNonNeg = 2,   // finite and not negative (the running sum l)
+  kCheckPositions = 3       // int32 positions: non-negative and strictly increasing
+};
+struct CheckItem {
+  const char* name;
+  const void* ptr;
+  int64_t n;      // elements
+  int32_t dtype;  // ra_dtype of the elements (unused for kCheckPositions)
+  int32_t kind;   // CheckKind
+};
+
+// counters[i] = number of elements of items[i] that break its rule, for
+// i < n_items (<= kMaxCheckItems); counters is device memory of n_items
+// words, cleared here by a kernel. Enqueued on `stream`.
+constexpr int kMaxCheckItems = 8;
+hipError_t launch_check_counts(const CheckItem* items, int n_items, unsigned long long* counters,
+                               hipStream_t stream);
+
 hipError_t launch_positions(int64_t seq_len, int32_t n_ranks, int32_t rank, int32_t layout,
                             int32_t* pos, hipStream_t stream);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
@@ -79,6 +101,7 @@ hipError_t launch_finalize(const float* o_acc, const float* m, const float* l, v
 hipError_t launch_bwd_delta(const void* o, const void* d_o, float* delta, int64_t rows,
                             int32_t head_dim, int32_t dtype, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_fp32(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t outer, int64_t len, int32_t d,
                        int32_t dtype, float base, hipStream_t stream);
 

@@ -18,11 +18,64 @@ __device__ __forceinline__ int perm_row(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// Chunk swizzle for a tile with 16 chunks of 16 bytes per row that is read
-// both by row (one 16-byte chunk per lane, rows perm_row(0..7) together) and
-// by the transposing read (4 consecutive rows x 32 bytes per 16-lane group):
-// either pattern touches distinct banks.
-__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+// LDS layout of a streamed tile of kTileRows rows of up to 128 bf16. The
+// tile is cut into 64-column halves, each stored as kTileRows rows of 128
+// bytes; 16-byte chunk cc (0..7) of row r of half h sits in slot
+// (h * kTileRows + r) * 8 + (cc ^ half_swz(r)).
+// The LDS has 64 banks of 4 bytes: two 128-byte rows fill them once, so rows
+// of equal parity share banks. A 16-byte read (ds_read_b128) is served 16
+// lanes at a time and an 8-byte transposing read 32 lanes at a time; both are
+// free of bank conflicts when the lanes served together touch 16 different
+// (row parity, chunk) slots.
+//  * Row fragments put 16 consecutive rows (a 16-row group in perm_row order)
+//    at one chunk in a 16-lane group: half_swz is a bijection on each parity
+//    class of a 16-row group.
+//  * Column fragments put 4 consecutive rows x 4 consecutive chunks in a
+//    32-lane group: half_swz separates rows r and r + 2 by chunk bit 2.
+// The swizzle depends only on a row's offset inside a 16-row group and never
+// crosses a half, so the half and the 16-row blocks of a fragment read fold
+// into the instruction's immediate offset, and each lane keeps only the byte
+// offsets of FragOffsets.
+constexpr int kTileRows = 64;
+__device__ __forceinline__ int half_swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+// Slot (16-byte unit) of chunk c (0 .. 15) of tile row r.
+__device__ __forceinline__ int tile_slot(int r, int c) {
+  return ((c >> 3) * kTileRows + r) * 8 + ((c & 7) ^ half_swz(r));
+}
+// Inverse: the tile row (in *r) and the chunk of the row held by slot p.
+__device__ __forceinline__ int tile_slot_chunk(int p, int* r) {
+  *r = (p >> 3) % kTileRows;
+  return ((p >> 3) / kTileRows) * 8 + ((p & 7) ^ half_swz(*r));
+}
+
+// Per-lane byte offsets of the two fragment kinds the MFMA kernels read.
+//  * row[m]: A operand of rows perm_row(lane % 32) of a 32-row block, k-step
+//    kk with kk % 4 == m (lane half hf holds chunk 2 * kk + hf). Rows r0 ..
+//    r0 + 31 (r0 a multiple of 32), k-step kk: tile + row[kk % 4] +
+//    (kk / 4) * kHalfBytes + r0 * 128.
+//  * col[half][d1]: transposing read of rows r0 + 8 * hf + 4 * half + i,
+//    i = 0..3, columns 32 * dt + 16 * ((lane / 16) % 2) + 4 * (lane % 4) ..
+//    + 3 with dt % 2 == d1; rows from r0 (a multiple of 16): tile +
+//    col[half][dt % 2] + (dt / 2) * kHalfBytes + r0 * 128.
+constexpr int kHalfBytes = kTileRows * 128;
+struct FragOffsets {
+  uint32_t row[4];
+  uint32_t col[2][2];
+  __device__ __forceinline__ explicit FragOffsets(int lane) {
+    const int l32 = lane & 31, hf = lane >> 5, g = (lane >> 4) & 1, j = lane & 15;
+    const int pr = perm_row(l32);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) row[m] = (uint32_t)tile_slot(pr, 2 * m + hf) * 16;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int d1 = 0; d1 < 2; ++d1) {
+        const int rl = 8 * hf + 4 * half + (j >> 2);
+        const int c = 4 * d1 + 2 * g + ((j & 3) >> 1);
+        col[half][d1] = (uint32_t)tile_slot(rl, c) * 16 + 8 * (j & 1);
+      }
+  }
+};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
@@ -49,11 +102,13 @@ __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfi
 // does not track the copy: it would otherwise wait for every copy in flight
 // before the next LDS read, including reads of the other buffer. Callers wait
 // for completion explicitly (s_waitcnt vmcnt(0)) before the barrier that
-// publishes the tile.
+// publishes the tile. The LDS address goes in through the "{m0}" operand: the
+// compiler itself loads m0 and knows the statement reads it (the statement
+// does not write m0). The s_nop separates that write from the copy, which
+// reads m0.
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ra_lds_void*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la)
-               : "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(la));
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane
@@ -66,25 +121,20 @@ __device__ __forceinline__ uint2 lds_tr4(const void* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// MFMA operand holding T[r0 + 8*hf + i][c0 + lane%32], i = 0..7, from a
-// row-major LDS tile of 128-element rows (16 chunks, tile_swz layout).
-__device__ __forceinline__ uint4 tile_col_frag(const uint4* tile, int r0, int c0, int lane) {
-  const int hf = lane >> 5, g = (lane >> 4) & 1, j = lane & 15;
-  const int col = c0 + 16 * g + 4 * (j & 3);
-  uint2 r2[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int r = r0 + 8 * hf + 4 * half + (j >> 2);
-    const int ch = (col >> 3) ^ tile_swz(r);
-    r2[half] = lds_tr4(reinterpret_cast<const char*>(&tile[r * 16 + ch]) + 2 * (col & 7));
-  }
-  return make_uint4(r2[0].x, r2[0].y, r2[1].x, r2[1].y);
+// The row fragment of rows r0 + perm_row(lane % 32), k-step kk (r0 a multiple
+// of 32).
+__device__ __forceinline__ uint4 tile_row_frag(const uint4* tile, int r0, int kk, const FragOffsets& f) {
+  const char* t = reinterpret_cast<const char*>(tile) + (kk >> 2) * kHalfBytes + r0 * 128;
+  return *reinterpret_cast<const uint4*>(t + f.row[kk & 3]);
 }
 
-// MFMA A operand for rows r0 + perm_row(lane%32) (one 16-byte chunk, k-step kk).
-__device__ __forceinline__ uint4 tile_row_frag(const uint4* tile, int r0, int kk, int lane) {
-  const int row = r0 + perm_row(lane & 31);
-  return tile[row * 16 + ((2 * kk + (lane >> 5)) ^ tile_swz(row))];
+// MFMA operand holding T[r0 + 8*hf + i][32*dt + lane%32], i = 0..7: two
+// transposing reads (r0 a multiple of 16).
+__device__ __forceinline__ uint4 tile_col_frag(const uint4* tile, int r0, int dt, const FragOffsets& f) {
+  const char* t = reinterpret_cast<const char*>(tile) + (dt >> 1) * kHalfBytes + r0 * 128;
+  const uint2 a0 = lds_tr4(t + f.col[0][dt & 1]);
+  const uint2 a1 = lds_tr4(t + f.col[1][dt & 1]);
+  return make_uint4(a0.x, a0.y, a1.x, a1.y);
 }
 
 }  // namespace ra

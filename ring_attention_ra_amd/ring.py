@@ -89,6 +89,10 @@ def forward(q_loc, k_ch, v_ch, pos, rank: int, causal: bool, scale: float, slope
     [B,Hq,C] (fp32)."""
     n = k_ch.shape[0]
     order = ring_schedule(n, rank) if chunks is None else list(chunks)
+    # A chunk folded in twice, or one out of range, would be counted wrongly
+    # without any error: every chunk is visited at most once.
+    if len(set(order)) != len(order) or not all(0 <= s < n for s in order):
+        raise ValueError(f"chunk order {order} must visit each of the {n} chunks at most once")
     state = State(_lib.dims_of(q_loc, k_ch[0]), q_loc.device, stream)
     for s in order:
         fold(state, q_loc, k_ch[s], v_ch[s], pos[rank], pos[s], causal, scale, slopes, stream)

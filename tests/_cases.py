@@ -3,7 +3,9 @@ through the C ABI, run the fp64 oracle on host copies of the same values."""
 
 from __future__ import annotations
 
+import json
 import math
+import os
 import sys
 import time
 from dataclasses import dataclass, field
@@ -93,6 +95,18 @@ def max_abs(a, b) -> float:
         d = np.where(same_inf, 0.0, np.abs(a - b))
     d = np.where(np.isnan(d), np.inf, d)
     return float(d.max())
+
+
+def record(config: str, rank: int, errors: dict, **extra) -> None:
+    """Append one JSON line (config, rank, error figures, seeds, versions) to
+    the file named by RA_PARITY_RECORD, when that is set."""
+    path = os.environ.get("RA_PARITY_RECORD")
+    if not path:
+        return
+    rec = {"config": config, "rank": int(rank), **{k: float(v) for k, v in errors.items()},
+           "torch": torch.__version__, "hip": getattr(torch.version, "hip", None), **extra}
+    with open(path, "a") as f:
+        f.write(json.dumps(rec) + "\n")
 
 
 class Timer:

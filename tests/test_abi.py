@@ -113,9 +113,13 @@ def test_rope_validation():
 
 
 def test_bwd_validation():
+    d = _dims(d=64)
+    args = [ctypes.byref(d)] + [None] * 5 + [1, 0.1, None] + [None] * 6 + [None]
+    assert L.ra_step_bwd(*args) == 2 and "head_dim 128" in _lib.ra_last_error()
+    d = _dims(dt=_lib.RA_FP32, d=129)
+    assert L.ra_step_bwd(ctypes.byref(d), *args[1:]) == 2 and "head_dim" in _lib.ra_last_error()
     d = _dims(dt=_lib.RA_FP32, d=64)
-    args = [ctypes.byref(d)] + [1] * 5 + [1, 0.1, None] + [1] * 6 + [None]
-    assert L.ra_step_bwd(*args) == 2 and "bf16" in _lib.ra_last_error()
+    assert L.ra_step_bwd(ctypes.byref(d), *args[1:]) == 1 and "NULL" in _lib.ra_last_error()
     d = _dims()
     args = [ctypes.byref(d)] + [1] * 5 + [1, 0.1, None] + [1] * 5 + [None, None]
     assert L.ra_step_bwd(*args) == 1
@@ -149,3 +153,54 @@ def test_workloads_match_their_names():
     w4, w6 = configs.get(4), configs.get(6)
     assert (w6.heads_q, w6.heads_kv, w6.seq_len, w6.layout, w6.alibi, w6.backward) == \
         (w4.heads_q, w4.heads_kv, w4.seq_len, w4.layout, True, True)
+
+
+# ---------------------------------------------------------------------------
+# size limits: every size the kernels cannot address is refused before any
+# launch. Every call passes NULL tensors: a refused size returns
+# RA_ERR_UNSUPPORTED, an accepted one fails the NULL check that follows the
+# limit checks, so nothing is ever launched.
+# ---------------------------------------------------------------------------
+
+def _bwd(dims, ptr=None):
+    return L.ra_step_bwd(ctypes.byref(dims), ptr, ptr, ptr, ptr, ptr, 1, 0.1, None, ptr, ptr, ptr, ptr, ptr, ptr,
+                         None)
+
+
+@pytest.mark.parametrize("d,limit", [(128, 4194304), (64, 8388608)])
+def test_step_fwd_bf16_slab_limit(d, limit):
+    # one head's fp32 o_acc slab (len_q * head_dim * 4 bytes) must stay below 2^31
+    assert limit * d * 4 == 2 ** 31
+    assert _fwd(_dims(d=d, lq=limit), ptr=None) == 2 and "slab" in _lib.ra_last_error()
+    assert _fwd(_dims(d=d, lq=limit - 1), ptr=None) == 1 and "NULL" in _lib.ra_last_error()
+    # the key length is addressed with 64-bit pointers in the forward step
+    assert _fwd(_dims(d=d, lkv=limit), ptr=None) == 1
+
+
+def test_step_bwd_slab_limits():
+    limit = 2 ** 31 // (128 * 2)  # q / d_o and k / v slabs of one head, bf16
+    assert _bwd(_dims(lq=limit)) == 2 and "q / d_o" in _lib.ra_last_error()
+    assert _bwd(_dims(lkv=limit)) == 2 and "k / v" in _lib.ra_last_error()
+    assert _bwd(_dims(lq=limit - 1, lkv=limit - 1), ptr=None) == 1 and "NULL" in _lib.ra_last_error()
+
+
+def test_grid_limits():
+    # batch x heads x row tiles must fit the int32 grid
+    assert _fwd(_dims(b=2 ** 16, hq=2 ** 8, hkv=1, lq=256 * 128), ptr=None) == 2 and "grid" in _lib.ra_last_error()
+    assert _fwd(_dims(b=2 ** 16, hq=2 ** 8, hkv=1, lq=32 * 256, dt=_lib.RA_FP32, d=64), ptr=None) == 2
+    assert _bwd(_dims(b=2 ** 16, hq=2 ** 8, hkv=1, lq=128 * 128)) == 2 and "grid" in _lib.ra_last_error()
+    assert _fwd(_dims(b=2 ** 16, hq=2 ** 7, hkv=1, lq=128), ptr=None) == 1
+
+
+def test_limits_do_not_apply_to_empty_work():
+    assert _fwd(_dims(lq=2 ** 30, b=0), ptr=None) == 0
+    assert _bwd(_dims(lq=2 ** 30, lkv=0), ptr=None) == 0
+
+
+def test_count_nonfinite_validation():
+    n = ctypes.c_int64(7)
+    assert L.ra_count_nonfinite(1, 4, 0, None, None) == 1 and "count" in _lib.ra_last_error()
+    assert L.ra_count_nonfinite(1, -1, 0, ctypes.byref(n), None) == 1
+    assert L.ra_count_nonfinite(1, 4, 9, ctypes.byref(n), None) == 1 and "dtype" in _lib.ra_last_error()
+    assert L.ra_count_nonfinite(None, 4, 0, ctypes.byref(n), None) == 1 and "NULL" in _lib.ra_last_error()
+    assert L.ra_count_nonfinite(None, 0, 0, ctypes.byref(n), None) == 0 and n.value == 0

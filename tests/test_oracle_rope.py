@@ -1,14 +1,17 @@
-"""Pins for the RoPE oracle, each independent of the oracle's own formula:
+"""Pins for the RoPE oracle, each independent of the oracle's own formula
+(which multiplies complex numbers):
 
-* the same rotation written as complex multiplication (numpy complex128),
+* each pair turned element by element in pure Python with math.cos / math.sin,
 * the same rotation as a block 2x2 rotation matrix applied with a matmul,
 * position 0 is the identity, and rotation preserves each pair's norm,
 * the rotation group law: rotating by a then by b equals rotating by a + b,
 * the relative-position property the page states: <R_m q, R_n k> depends on
   m - n only,
-* a planted mistake (sine sign flipped, or the halves paired as neighbours)
-  fails the complex-number pin.
+* a planted mistake (sine sign flipped, the halves paired as neighbours, or
+  the frequency exponent off by one pair) fails the element-by-element pin.
 """
+
+import math
 
 import numpy as np
 import pytest
@@ -21,17 +24,24 @@ def _rand(shape, seed):
     return np.random.default_rng(seed).normal(size=shape)
 
 
+POSITIONS = [0, 1, 2, 5, 63, 64, 100, 1000, 4095, 4096, 65535, 131071, 200000, 524287, 1048575, 1048576, 999999]
+
+
 @pytest.mark.parametrize("d", [2, 8, 64, 128])
-def test_matches_complex_multiplication(d):
-    x = _rand((3, 17, d), 1)
-    pos = np.array([0, 1, 2, 5, 63, 64, 100, 1000, 4095, 4096, 65535, 131071, 200000, 524287, 1048575,
-                    1048576, 999999])
-    got = oracle.rotary_embedding(x, pos)
-    z = x[..., : d // 2] + 1j * x[..., d // 2:]
-    theta = 10000.0 ** (-(2.0 * np.arange(d // 2)) / d)
-    w = z * np.exp(1j * np.outer(pos, theta))
-    ref = np.concatenate([w.real, w.imag], axis=-1)
-    assert np.max(np.abs(got - ref)) < 1e-9
+def test_matches_elementwise_rotation(d):
+    x = _rand((2, len(POSITIONS), d), 1)
+    got = oracle.rotary_embedding(x, np.array(POSITIONS))
+    h = d // 2
+    worst = 0.0
+    for b in range(x.shape[0]):
+        for t, p in enumerate(POSITIONS):
+            for j in range(h):
+                a = p * math.pow(10000.0, -2.0 * j / d)
+                c, s_ = math.cos(a), math.sin(a)
+                x1, x2 = float(x[b, t, j]), float(x[b, t, j + h])
+                worst = max(worst, abs(got[b, t, j] - (x1 * c - x2 * s_)),
+                            abs(got[b, t, j + h] - (x1 * s_ + x2 * c)))
+    assert worst < 1e-9
 
 
 def test_matches_rotation_matrices():
@@ -74,21 +84,25 @@ def test_relative_position_property():
         assert abs(dot - ref) < 1e-9 * (1 + abs(ref))
 
 
-@pytest.mark.parametrize("mistake", ["sine_sign", "neighbour_pairs"])
+@pytest.mark.parametrize("mistake", ["sine_sign", "neighbour_pairs", "exponent"])
 def test_planted_mistakes_are_caught(monkeypatch, mistake):
+    true_rope = rope_fp64.rotary_embedding
+
     def flawed(x, positions, base=10000.0):
         x = np.asarray(x, dtype=np.float64)
         d = x.shape[-1]
-        ang = np.asarray(positions, dtype=np.float64)[:, None] * rope_fp64.inv_freq(d, base)[None, :]
-        cos, sin = np.cos(ang), np.sin(ang)
         if mistake == "sine_sign":
-            x1, x2 = x[..., : d // 2], x[..., d // 2:]
-            return np.concatenate([x1 * cos + x2 * sin, -x1 * sin + x2 * cos], axis=-1)
-        x1, x2 = x[..., 0::2], x[..., 1::2]
+            return true_rope(x, -np.asarray(positions), base)
+        if mistake == "exponent":  # theta_j = base^(-2(j+1)/d): every plane one step too slow
+            h = d // 2
+            theta = base ** (-2.0 * (np.arange(h) + 1.0) / d)
+            w = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * np.multiply.outer(np.asarray(positions, float), theta))
+            return np.concatenate([w.real, w.imag], axis=-1)
         out = np.empty_like(x)
-        out[..., 0::2], out[..., 1::2] = x1 * cos - x2 * sin, x1 * sin + x2 * cos
+        nb = true_rope(np.concatenate([x[..., 0::2], x[..., 1::2]], axis=-1), positions, base)
+        out[..., 0::2], out[..., 1::2] = nb[..., : d // 2], nb[..., d // 2:]
         return out
 
     monkeypatch.setattr(oracle, "rotary_embedding", flawed)
     with pytest.raises(AssertionError):
-        test_matches_complex_multiplication(8)
+        test_matches_elementwise_rotation(8)

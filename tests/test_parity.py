@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from ring_attention_ra_amd import _lib, configs, ring
-from tests._cases import Case, Timer, draw, host64, host_heads, log, max_abs, oracle_slopes
+from tests._cases import Case, Timer, draw, host64, host_heads, log, max_abs, oracle_slopes, record
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,7 @@ def _check_full(case, ranks=None):
             [oracle.rank_positions(case.seq_len, case.n_ranks, i, case.layout) for i in range(case.n_ranks)]))
         eo, el = max_abs(host64(o), o_ref), max_abs(host64(lse), lse_ref)
         log(f"  rank {r}: max|dO|={eo:.3g} max|dLSE|={el:.3g}")
+        record(case.tag(), r, {"max_abs_O": eo, "max_abs_LSE": el})
         assert eo <= tol_o and el <= tol_l, (r, eo, el)
 
 
@@ -152,6 +153,14 @@ def test_fwd_bf16_tile_range_edges(layout, causal, alibi, hq, hkv, n, c):
     _check_full(Case("bf16", 1, hq, hkv, 128, n * c, n, layout, causal, alibi, seed=25))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("scale", [0.0, -0.06])
+def test_fwd_scale_zero_and_negative_with_alibi(dtype, scale):
+    # With scale <= 0 the fast paths that rely on scale > 0 are not taken.
+    _check_full(Case(dtype, 1, 4, 2, 128 if dtype == "bf16" else 64, 3 * 320, 3, "zigzag", True, True, seed=27,
+                     scale=scale))
+
+
 def test_fwd_bf16_batch2_and_std():
     _check_full(Case("bf16", 2, 3, 1, 128, 4 * 256, 4, "zigzag", True, True, std=0.7, seed=23))
 
@@ -193,23 +202,25 @@ def test_state_after_partial_ring():
         assert np.all(np.isneginf(host64(state.m)[empty])) and np.all(host64(state.l)[empty] == 0)
 
 
-def test_workload_16k_zigzag_two_ranks_full():
+def test_workload_16k_zigzag_all_ranks_full():
     w = configs.get(2)
     case = Case("bf16", w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seq_len, w.n_ranks, w.layout,
                 seed=w.index)
-    _check_full(case, ranks=[0, w.n_ranks - 1])
+    _check_full(case)
 
 
-def _sampled_full_size(w, n_rows=48, heads=None):
-    """Full-size run of a workload (the benchmark's launch configuration);
-    the oracle recomputes a sample of rows and heads one by one."""
+def _sampled_full_size(w, n_rows=48, heads=None, rank=None):
+    """Full-size run of a workload (the benchmark's launch configuration) for
+    one rank (the workload's own by default); the oracle recomputes a sample
+    of rows and heads one by one."""
+    rank = w.rank if rank is None else rank
     case = Case(w.dtype, w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seq_len, w.n_ranks, w.layout,
                 w.causal, w.alibi, w.std, seed=w.index)
-    log(f"case {w.name} (sampled)")
+    log(f"case {w.name} rank {rank} (sampled)")
     with Timer("draw + GPU ring"):
         q, k, v = draw(case)
-        res = _run_gpu(case, [w.rank], q, k, v)
-    o, lse, _ = res[w.rank]
+        res = _run_gpu(case, [rank], q, k, v)
+    o, lse, _ = res[rank]
     c = w.chunk
     rng = np.random.default_rng(w.index)
     rows = np.unique(np.concatenate([np.arange(16), np.arange(c - 16, c), rng.integers(0, c, n_rows - 32)]))
@@ -221,28 +232,34 @@ def _sampled_full_size(w, n_rows=48, heads=None):
         kh = host_heads(k, [h // g for h in heads])
         vh = host_heads(v, [h // g for h in heads])
     with Timer("oracle"):
-        o_ref, lse_ref = oracle.attention_rank_share(qh, kh, vh, w.n_ranks, w.rank, w.layout, w.causal, w.scale,
+        o_ref, lse_ref = oracle.attention_rank_share(qh, kh, vh, w.n_ranks, rank, w.layout, w.causal, w.scale,
                                                      oracle_slopes(case), rows=rows, heads=heads)
     o_g = host64(o[:, heads][:, :, rows])
     l_g = host64(lse[:, heads][:, :, rows])
     eo, el = max_abs(o_g, o_ref), max_abs(l_g, lse_ref)
     log(f"  rows={rows.size} heads={heads}: max|dO|={eo:.3g} max|dLSE|={el:.3g}")
+    record(w.name, rank, {"max_abs_O": eo, "max_abs_LSE": el}, sample=f"{rows.size} rows x heads {heads}")
     tol_o, tol_l = TOL[w.dtype]
     assert eo <= tol_o and el <= tol_l
     # a property that holds at any size: every output is finite
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
-def test_workload_128k_zigzag_sampled():
-    _sampled_full_size(configs.get(3))
+@pytest.mark.parametrize("rank", [0, 7])
+def test_workload_128k_zigzag_sampled(rank):
+    _sampled_full_size(configs.get(3), rank=rank)
 
 
-def test_workload_64k_gqa_alibi_sampled():
-    _sampled_full_size(configs.get(4))
+@pytest.mark.parametrize("rank", [0, 3])
+def test_workload_64k_gqa_alibi_sampled(rank):
+    _sampled_full_size(configs.get(4), rank=rank)
 
 
-def test_workload_1m_zigzag_forward_sampled():
-    _sampled_full_size(configs.get(5), heads=[0, 15])
+@pytest.mark.parametrize("rank", [0, 63])
+def test_workload_1m_zigzag_forward_sampled(rank):
+    # Under zig-zag, rank 0's first row (position 0) sees no key in any chunk
+    # but its own: every later step has a row with no visible key.
+    _sampled_full_size(configs.get(5), heads=[0, 15], rank=rank)
 
 
 # ---------------------------------------------------------------------------
@@ -306,7 +323,8 @@ def test_fp32_finalize_of_unvisited_rows():
 
 
 # ---------------------------------------------------------------------------
-# backward parity (bf16, D = 128): max |g - g_ref| <= 1e-2 * max |g_ref|
+# backward parity: bf16 (D = 128) max |g - g_ref| <= 1e-2 * max |g_ref|;
+# fp32 max |g - g_ref| <= 1e-5 * max(1, max |g_ref|)
 # ---------------------------------------------------------------------------
 
 BWD_REL = 1e-2
@@ -348,7 +366,84 @@ def test_bwd_variants(layout, causal, alibi, hq, hkv, n, c):
         e_k = _rel_err(host64(dk), oracle.permute_to_ranks(dk_r, n, layout))
         e_v = _rel_err(host64(dv), oracle.permute_to_ranks(dv_r, n, layout))
         log(f"  rank {r}: rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g}")
+        record(case.tag(), r, {"rel_dQ": e_q, "rel_dK": e_k, "rel_dV": e_v})
         assert e_q <= BWD_REL and e_k <= BWD_REL and e_v <= BWD_REL
+
+
+@pytest.mark.parametrize("layout,alibi,hq,hkv,n,c,ranks", [
+    # 16K zig-zag over 8 chunks of 2048: a key's dK / dV sums over up to 2048
+    # rows of the rank's chunk, every row and key compared.
+    ("zigzag", False, 2, 2, 8, 2048, (0, 7)),
+    # contiguous GQA 8/2 + ALiBi: the last rank's keys of chunk 0 are summed over
+    # all 2048 rows of each of the 4 query heads that share their K/V head.
+    ("contiguous", True, 8, 2, 4, 2048, (0, 3)),
+])
+def test_bwd_long_sums_full(layout, alibi, hq, hkv, n, c, ranks):
+    case = Case("bf16", 1, hq, hkv, 128, n * c, n, layout, True, alibi, seed=65)
+    log(f"case {case.tag()}")
+    q, k, v, do = draw(case, with_do=True)
+    qh, kh, vh = host64(q), host64(k), host64(v)
+    for r in ranks:
+        with Timer(f"rank {r} GPU"):
+            dq, dk, dv = _bwd_gpu(case, r, q, k, v, do)
+        with Timer(f"rank {r} oracle"):
+            dq_r, dk_r, dv_r = oracle.attention_rank_share_bwd(qh, kh, vh, host64(do), n, r, layout, True,
+                                                               case.sc(), oracle_slopes(case))
+        e_q = _rel_err(host64(dq), dq_r)
+        e_k = _rel_err(host64(dk), oracle.permute_to_ranks(dk_r, n, layout))
+        e_v = _rel_err(host64(dv), oracle.permute_to_ranks(dv_r, n, layout))
+        log(f"  rank {r}: rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g}")
+        record(case.tag(), r, {"rel_dQ": e_q, "rel_dK": e_k, "rel_dV": e_v})
+        assert e_q <= BWD_REL and e_k <= BWD_REL and e_v <= BWD_REL
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.06])
+def test_bwd_scale_zero_and_negative_with_alibi(scale):
+    # The linear form of the ALiBi term divides by the scale; scale <= 0 takes
+    # the per-element path.
+    case = Case("bf16", 1, 4, 2, 128, 2 * 320, 2, "zigzag", True, True, seed=67, scale=scale)
+    log(f"case {case.tag()} scale={scale}")
+    q, k, v, do = draw(case, with_do=True)
+    qh, kh, vh = host64(q), host64(k), host64(v)
+    for r in (0, 1):
+        dq, dk, dv = _bwd_gpu(case, r, q, k, v, do)
+        dq_r, dk_r, dv_r = oracle.attention_rank_share_bwd(qh, kh, vh, host64(do), 2, r, "zigzag", True, scale,
+                                                           oracle_slopes(case))
+        e_q = _rel_err(host64(dq), dq_r)
+        e_k = _rel_err(host64(dk), oracle.permute_to_ranks(dk_r, 2, "zigzag"))
+        e_v = _rel_err(host64(dv), oracle.permute_to_ranks(dv_r, 2, "zigzag"))
+        log(f"  rank {r}: rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g}")
+        assert np.isfinite(e_q) and e_q <= BWD_REL and e_k <= BWD_REL and e_v <= BWD_REL
+
+
+def _abs_err_scaled(got, ref):
+    return max_abs(got, ref) / max(1.0, float(np.max(np.abs(ref))) if ref.size else 0.0)
+
+
+BWD_FP32 = 1e-5  # max |g - g_ref| <= 1e-5 * max(1, max |g_ref|)
+
+
+@pytest.mark.parametrize("layout,causal,alibi,hq,hkv,d,n,c", [
+    ("contiguous", True, False, 1, 1, 64, 4, 64),     # the fp32 workload's shape, every rank
+    ("zigzag", True, True, 4, 2, 33, 3, 70),          # ALiBi + GQA, ragged D and lengths
+    ("contiguous", False, True, 2, 1, 100, 2, 45),    # no mask
+    ("zigzag", True, False, 2, 2, 128, 2, 96),
+])
+def test_bwd_fp32(layout, causal, alibi, hq, hkv, d, n, c):
+    case = Case("fp32", 1, hq, hkv, d, n * c, n, layout, causal, alibi, seed=69)
+    log(f"case {case.tag()}")
+    q, k, v, do = draw(case, with_do=True)
+    qh, kh, vh = host64(q), host64(k), host64(v)
+    for r in range(n):
+        dq, dk, dv = _bwd_gpu(case, r, q, k, v, do)
+        dq_r, dk_r, dv_r = oracle.attention_rank_share_bwd(qh, kh, vh, host64(do), n, r, layout, causal, case.sc(),
+                                                           oracle_slopes(case))
+        e_q = _abs_err_scaled(host64(dq), dq_r)
+        e_k = _abs_err_scaled(host64(dk), oracle.permute_to_ranks(dk_r, n, layout))
+        e_v = _abs_err_scaled(host64(dv), oracle.permute_to_ranks(dv_r, n, layout))
+        log(f"  rank {r}: dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g} (x max(1, max|g|))")
+        record(case.tag(), r, {"scaled_dQ": e_q, "scaled_dK": e_k, "scaled_dV": e_v})
+        assert e_q <= BWD_FP32 and e_k <= BWD_FP32 and e_v <= BWD_FP32
 
 
 def test_bwd_deterministic():
