@@ -205,6 +205,19 @@ ra_status ra_step_bwd(const ra_dims* d, const void* q, const void* k_blk, const 
  * with n > 0, unknown dtype. */
 ra_status ra_count_nonfinite(const void* x, int64_t n, int32_t dtype, int64_t* count, void* stream);
 
+/* ra_count_nonfinite without any allocation, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid it).
+ * Same arguments, result and errors. Its counter lives in a 64-byte static
+ * device array of the library (one copy per GPU, held until the process
+ * ends, found through hipGetSymbolAddress once per device), not in memory
+ * allocated per call; n may take any value, since one 64-bit counter serves
+ * any size. Every call on a GPU shares that array, which is cleared at the
+ * start of each call: calls that overlap on one GPU (several host threads,
+ * or streams running concurrently) race and may return wrong counts. Uses
+ * the current device; `stream` must belong to it. */
+ra_status ra_count_nonfinite_noalloc(const void* x, int64_t n, int32_t dtype, int64_t* count,
+                                     void* stream);
+
 /* Text for the last non-OK status returned on this host thread ("" if none). */
 const char* ra_last_error(void);
 

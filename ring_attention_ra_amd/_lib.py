@@ -57,6 +57,7 @@ _SIGNATURES = {
     "ra_bwd_delta": [_DIMS, _P, _P, _P, _P],
     "ra_step_bwd": [_DIMS, _P, _P, _P, _P, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
     "ra_count_nonfinite": [_P, _I64, _I32, ctypes.POINTER(ctypes.c_int64), _P],
+    "ra_count_nonfinite_noalloc": [_P, _I64, _I32, ctypes.POINTER(ctypes.c_int64), _P],
     "ra_last_error": [],
     "ra_abi_version": [],
 }
@@ -228,6 +229,15 @@ def ra_count_nonfinite(x, stream=None) -> int:
     n = ctypes.c_int64(-1)
     _check(lib().ra_count_nonfinite(_ptr(x, "x"), x.numel(), dtype_code(x.dtype), ctypes.byref(n),
                                     _stream(stream)), "ra_count_nonfinite")
+    return int(n.value)
+
+
+def ra_count_nonfinite_noalloc(x, stream=None) -> int:
+    """ra_count_nonfinite through the library's static scratch counter (no
+    device allocation; calls that overlap on one GPU race)."""
+    n = ctypes.c_int64(-1)
+    _check(lib().ra_count_nonfinite_noalloc(_ptr(x, "x"), x.numel(), dtype_code(x.dtype), ctypes.byref(n),
+                                            _stream(stream)), "ra_count_nonfinite_noalloc")
     return int(n.value)
 
 

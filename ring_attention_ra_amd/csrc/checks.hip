@@ -9,9 +9,20 @@
 // receives (discosf.com article, §5.2 典型问题排查, NaN loss and ring transfer
 // corruption). These checks are HBM-bound reductions; they are not on the hot
 // path and run only when asked for.
+#include <mutex>
+#include <vector>
+
 #include "ra_internal.h"
 
 namespace ra {
+
+// Scratch of ra_count_nonfinite_noalloc: kMaxCheckItems 64-bit counters in a
+// file-scope device array (64 bytes), for callers that cannot allocate. Each
+// GPU the library runs on holds its own copy at its own address until the
+// process ends, and every call on that GPU shares it: the counters are
+// cleared at the start of each use, and calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned long long scratch[kMaxCheckItems];
+
 namespace {
 
 // True when an element breaks the rule of its check kind, from its raw bits.
@@ -70,6 +81,27 @@ unsigned grid_for(int64_t n) {
 }
 
 }  // namespace
+
+// Device address of `scratch` on the current device. In host code the array's
+// name is only a stand-in: the address comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and is kept per device.
+hipError_t scratch_counters(unsigned long long** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::vector<unsigned long long*> per_device;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)per_device.size() <= dev) per_device.resize(dev + 1, nullptr);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = static_cast<unsigned long long*>(p);
+  }
+  *out = per_device[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_check_counts(const CheckItem* items, int n_items, unsigned long long* counters,
                                hipStream_t stream) {

@@ -107,20 +107,16 @@ static bool env_on(const char* name) {
   return v && v[0] && strcmp(v, "0") != 0;
 }
 
-// Runs the checks of items[0 .. n) on `stream`, waits for them, and returns
-// RA_OK or `bad_status` naming the first item that failed. Holds a small
-// device counter array for the duration of the call.
-static ra_status run_checks(const CheckItem* items, int n, hipStream_t stream, const char* entry,
-                            const char* when, ra_status bad_status, int64_t* counts_out = nullptr) {
-  unsigned long long* dev = nullptr;
-  hipError_t e = hipMalloc(&dev, kMaxCheckItems * sizeof(unsigned long long));
-  if (e != hipSuccess) return launch_result(e, "check counters");
+// Runs the checks of items[0 .. n) on `stream` with the device counters
+// `dev`, waits for them, and returns RA_OK or `bad_status` naming the first
+// item that failed (or, with counts_out, the counts of every item).
+static ra_status run_checks_with(unsigned long long* dev, const CheckItem* items, int n, hipStream_t stream,
+                                 const char* entry, const char* when, ra_status bad_status,
+                                 int64_t* counts_out) {
   unsigned long long host[kMaxCheckItems] = {};
-  e = launch_check_counts(items, n, dev, stream);
+  hipError_t e = launch_check_counts(items, n, dev, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(host, dev, n * sizeof(unsigned long long), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  const hipError_t ef = hipFree(dev);
-  if (e == hipSuccess) e = ef;
   if (e != hipSuccess) return launch_result(e, "device check");
   for (int i = 0; i < n; ++i) {
     if (counts_out) counts_out[i] = (int64_t)host[i];
@@ -134,6 +130,18 @@ static ra_status run_checks(const CheckItem* items, int n, hipStream_t stream, c
                 when);
   }
   return RA_OK;
+}
+
+// The same with a device counter array allocated for the call.
+static ra_status run_checks(const CheckItem* items, int n, hipStream_t stream, const char* entry,
+                            const char* when, ra_status bad_status, int64_t* counts_out = nullptr) {
+  unsigned long long* dev = nullptr;
+  hipError_t e = hipMalloc(&dev, kMaxCheckItems * sizeof(unsigned long long));
+  if (e != hipSuccess) return launch_result(e, "check counters");
+  const ra_status st = run_checks_with(dev, items, n, stream, entry, when, bad_status, counts_out);
+  e = hipFree(dev);
+  if (st == RA_OK && e != hipSuccess) return launch_result(e, "check counters");
+  return st;
 }
 
 static CheckItem item(const char* name, const void* p, int64_t n, int32_t dtype, int32_t kind) {
@@ -387,6 +395,21 @@ ra_status ra_count_nonfinite(const void* x, int64_t n, int32_t dtype, int64_t* c
   if (!x) return fail(RA_ERR_INVALID_ARGUMENT, "x is NULL");
   const CheckItem it[] = {item("x", x, n, dtype, kCheckFinite)};
   return run_checks(it, 1, (hipStream_t)stream, "ra_count_nonfinite", "", RA_ERR_NONFINITE, count);
+}
+
+ra_status ra_count_nonfinite_noalloc(const void* x, int64_t n, int32_t dtype, int64_t* count, void* stream) {
+  if (!count) return fail(RA_ERR_INVALID_ARGUMENT, "count is NULL");
+  if (n < 0) return fail(RA_ERR_INVALID_ARGUMENT, "n must be non-negative");
+  if (!dtype_ok(dtype)) return fail(RA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  *count = 0;
+  if (n == 0) return RA_OK;
+  if (!x) return fail(RA_ERR_INVALID_ARGUMENT, "x is NULL");
+  unsigned long long* dev = nullptr;
+  const hipError_t e = scratch_counters(&dev);
+  if (e != hipSuccess) return launch_result(e, "scratch counters");
+  const CheckItem it[] = {item("x", x, n, dtype, kCheckFinite)};
+  return run_checks_with(dev, it, 1, (hipStream_t)stream, "ra_count_nonfinite_noalloc", "", RA_ERR_NONFINITE,
+                         count);
 }
 
 }  // extern "C"

@@ -87,6 +87,9 @@ struct CheckItem {
 constexpr int kMaxCheckItems = 8;
 hipError_t launch_check_counts(const CheckItem* items, int n_items, unsigned long long* counters,
                                hipStream_t stream);
+// Device address of the library's static scratch counters (kMaxCheckItems
+// words) on the current device; no allocation.
+hipError_t scratch_counters(unsigned long long** out);
 
 hipError_t launch_positions(int64_t seq_len, int32_t n_ranks, int32_t rank, int32_t layout,
                             int32_t* pos, hipStream_t stream);
