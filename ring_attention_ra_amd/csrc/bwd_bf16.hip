@@ -144,17 +144,12 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
   const int kmax_w = wave_active ? a.k_pos[min(kw0 + 31, Lkv - 1)] : INT32_MAX;
   const int kmin_wg = a.k_pos[k0];
 
-  // First query that can see any key of the work-group (positions increase).
-  int qstart = 0;
-  if (causal) {
-    int lo = 0, hi = Lq;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a.q_pos[mid] < kmin_wg) lo = mid + 1; else hi = mid;
-    }
-    qstart = lo;
-  }
-  const int qt0 = qstart / TROWS;
+  // First query tile that can see a key of the work-group: the tiles before
+  // it end below the work-group's first key (positions increase).
+  int qt0 = 0;
+  if (causal)
+    qt0 = prefix_count((Lq + TROWS - 1) / TROWS, lane,
+                       [&](int u) { return a.q_pos[min(u * TROWS + TROWS - 1, Lq - 1)] < kmin_wg; });
   const int nq = (Lq + TROWS - 1) / TROWS - qt0;
   const int n_items = nq > 0 ? g * nq : 0;
 

@@ -94,13 +94,6 @@ constexpr float kLimit = 16384.0f;  // bound on a lane's per-tile sum of P (> 32
 
 enum TileMode { kFast = 0, kAlibiLinear = 1, kExact = 2 };
 
-// 4 bytes per lane from global memory into LDS at lds_base + 4*lane (issued
-// like dma16: untracked by the compiler, awaited explicitly).
-__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
-  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ra_lds_void*)lds_base);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(la));
-}
-
 // Scheduling pattern of one MFMA phase: NQK QK products (one LDS read each)
 // followed by NPV P.V products (two transposing LDS reads each). The reads of
 // the first four products go first; after product i come the reads of

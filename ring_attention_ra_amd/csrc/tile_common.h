@@ -97,6 +97,26 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Number of u in [0, n) for which pred(u) holds, where pred holds on a prefix
+// of [0, n) (it is monotone, e.g. a comparison against increasing
+// positions). A 64-way search: each round every lane of the (fully active)
+// wave probes one evenly spaced u of the remaining range, and the ballot of
+// the answers narrows the range to less than the probe spacing, so a range
+// of n takes about log64(n) rounds of one load per lane.
+template <typename Pred>
+__device__ __forceinline__ int prefix_count(int n, int lane, Pred pred) {
+  int lo = 0, hi = n;  // the count lies in [lo, hi]
+  while (lo < hi) {
+    const int step = (hi - lo + 63) >> 6;
+    const int p = lo + lane * step;
+    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(p < hi && pred(p)));
+    const int nlo = cnt > 0 ? lo + (cnt - 1) * step + 1 : lo;
+    hi = min(hi, lo + cnt * step);
+    lo = nlo;
+  }
+  return lo;
+}
+
 // 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane
 // (lds_base is wave-uniform). Issued from inline assembly so that the compiler
 // does not track the copy: it would otherwise wait for every copy in flight
@@ -109,6 +129,13 @@ __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfi
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ra_lds_void*)lds_base);
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(la));
+}
+
+// 4 bytes per lane from global memory into LDS at lds_base + 4*lane (issued
+// like dma16: untracked by the compiler, awaited explicitly).
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ra_lds_void*)lds_base);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(la));
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane
