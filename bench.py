@@ -121,6 +121,15 @@ def clock_window(step, reader, seconds, ms_per_step):
             "source": "amdsmi gpu metrics (current_gfxclks), untimed steps after the timed region"}
 
 
+def kernel_source_sha256(source):
+    """sha256 of a kernel source file followed by the shared tile header it includes."""
+    h = hashlib.sha256()
+    for name in (source, "tile_common.h"):
+        with open(os.path.join(ROOT, "ring_attention_ra_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def visible_pairs_per_chunk(w, pos_cpu):
     """Visible (query, key) pairs per head for each ring step of the rank."""
     qp = pos_cpu[w.rank]
@@ -339,8 +348,7 @@ def main():
             return None
         with open(args.traffic) as f:
             recs = json.load(f).get("records", [])
-        with open(os.path.join(ROOT, "ring_attention_ra_amd", "csrc", source), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha256(source)
         for rec in recs:
             if rec.get("kernel") == kernel and rec.get("workload") == w.name and \
                     rec.get("kernel_source_sha256") == sha:
