@@ -377,6 +377,9 @@ def test_bwd_variants(layout, causal, alibi, hq, hkv, n, c):
     # contiguous GQA 8/2 + ALiBi: the last rank's keys of chunk 0 are summed over
     # all 2048 rows of each of the 4 query heads that share their K/V head.
     ("contiguous", True, 8, 2, 4, 2048, (0, 3)),
+    # one 16384-row chunk attending to itself: the dK / dV of key 0 is a sum
+    # over all 16384 rows, the length of a full-size chunk.
+    ("contiguous", False, 1, 1, 1, 16384, (0,)),
 ])
 def test_bwd_long_sums_full(layout, alibi, hq, hkv, n, c, ranks):
     case = Case("bf16", 1, hq, hkv, 128, n * c, n, layout, True, alibi, seed=65)
@@ -490,6 +493,8 @@ def test_workload_gqa_alibi_contiguous_backward_sampled():
     dq_g = host64(dq[:, qheads][:, :, rows])
     e_q, e_k, e_v = _rel_err(dq_g, dq_r), _rel_err(dk_g, dk_r), _rel_err(dv_g, dv_r)
     log(f"  rows={rows.size} keys={keys.size}: rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g}")
+    record(w.name, w.rank, {"rel_dQ": e_q, "rel_dK": e_k, "rel_dV": e_v},
+           sample=f"{rows.size} rows, {keys.size} keys")
     assert e_q <= BWD_REL and e_k <= BWD_REL and e_v <= BWD_REL
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
 
@@ -526,5 +531,7 @@ def test_workload_1m_zigzag_backward_sampled():
     dq_g = host64(dq[:, heads][:, :, rows])
     e_q, e_k, e_v = _rel_err(dq_g, dq_r), _rel_err(dk_g, dk_r), _rel_err(dv_g, dv_r)
     log(f"  rows={rows.size} keys={keys.size}: rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g}")
+    record(w.name, w.rank, {"rel_dQ": e_q, "rel_dK": e_k, "rel_dV": e_v},
+           sample=f"{rows.size} rows, {keys.size} keys")
     assert e_q <= BWD_REL and e_k <= BWD_REL and e_v <= BWD_REL
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
