@@ -25,10 +25,11 @@ dominates there. It also carries the step's algorithmic HBM bytes per launch
 and the rate they imply. `cpu_baseline` is the fp64 oracle timed on a bounded
 sample of the same workload on the host cores. `breakdown` adds the layout
 permutation's rate, the backward at 8*D per pair (without the recomputed S)
-next to the 10*D figure, the shader clock read from the device over untimed
-steps run after the timed region (with the peak scaled to it), and the rotary
-position embedding
-of the rank's K chunks, timed after the step as a separate pass.
+next to the 10*D figure, the shader clock and socket power read from the
+device over untimed steps run after the timed region (with the peak scaled to
+the clock, the power cap, and the fraction of the window in which the package
+power limit was holding the clock down), and the rotary position embedding of
+the rank's K chunks, timed after the step as a separate pass.
 """
 
 from __future__ import annotations
@@ -78,6 +79,7 @@ class ClockReader:
             self._api = None
 
     def read(self):
+        """(shader clock MHz, socket power W or None), or None."""
         if self._api is None:
             return None
         try:
@@ -86,21 +88,50 @@ class ClockReader:
             return None
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 10000]
         if clks:
-            return sum(clks) / len(clks)
-        c = m.get("current_gfxclk")
-        return float(c) if isinstance(c, int) and 0 < c < 10000 else None
+            mhz = sum(clks) / len(clks)
+        else:
+            c = m.get("current_gfxclk")
+            if not (isinstance(c, int) and 0 < c < 10000):
+                return None
+            mhz = float(c)
+        pw = m.get("current_socket_power")
+        return mhz, (float(pw) if isinstance(pw, int) and 0 < pw < 100000 else None)
+
+    def power_cap_w(self):
+        if self._api is None:
+            return None
+        try:
+            cap = self._api.amdsmi_get_power_cap_info(self._handle).get("power_cap")
+        except Exception:  # noqa: BLE001
+            return None
+        return cap / 1e6 if isinstance(cap, int) and cap > 0 else None
+
+    def ppt_counters(self):
+        """(accumulation counter, of which with the package power limit
+        active), from the device's violation status; None if unavailable."""
+        if self._api is None:
+            return None
+        try:
+            v = self._api.amdsmi_get_violation_status(self._handle)
+        except Exception:  # noqa: BLE001
+            return None
+        acc, ppt = v.get("acc_counter"), v.get("acc_ppt_pwr")
+        return (acc, ppt) if isinstance(acc, int) and isinstance(ppt, int) else None
 
 
 def clock_window(step, reader, seconds, ms_per_step):
-    """The shader clock under the same load: after the timed region, run
-    untimed steps for about `seconds`, keeping two steps in flight, and read
-    the clock after each (the metrics table refreshes a few times per second,
-    so one sample is kept per distinct reading)."""
+    """The shader clock and socket power under the same load: after the timed
+    region, run untimed steps for about `seconds`, keeping two steps in
+    flight, and read the clock and power after each (the metrics table
+    refreshes a few times per second: the clock is averaged over its distinct
+    readings, the power over all of them); plus the fraction of the window in
+    which the package power limit was holding the clock down."""
     if reader.read() is None:
         return None
     n = max(20, int(seconds * 1e3 / max(ms_per_step, 1e-3)))
     done = []
     samples = []
+    ppt0 = ppt1 = None
     for i in range(n):
         step(False)
         ev = torch.cuda.Event()
@@ -111,14 +142,27 @@ def clock_window(step, reader, seconds, ms_per_step):
             v = reader.read()
             if v is not None:
                 samples.append(v)
+        if i == n // 5:
+            ppt0 = reader.ppt_counters()
+    ppt1 = reader.ppt_counters()
     torch.cuda.synchronize()
     if not samples:
         return None
     body = samples[len(samples) // 5:]  # the first reads may predate the load
     distinct = [v for k, v in enumerate(body) if k == 0 or v != body[k - 1]]
-    return {"gfx_mhz_mean": round(statistics.fmean(distinct), 1), "gfx_mhz_min": round(min(distinct), 1),
-            "gfx_mhz_max": round(max(distinct), 1), "readings": len(distinct), "window_steps": n,
-            "source": "amdsmi gpu metrics (current_gfxclks), untimed steps after the timed region"}
+    mhz = [v[0] for v in distinct]
+    watts = [v[1] for v in body if v[1] is not None]
+    out = {"gfx_mhz_mean": round(statistics.fmean(mhz), 1), "gfx_mhz_min": round(min(mhz), 1),
+           "gfx_mhz_max": round(max(mhz), 1), "readings": len(distinct), "window_steps": n,
+           "source": "amdsmi gpu metrics (current_gfxclks, current_socket_power) and violation status, "
+                     "untimed steps after the timed region"}
+    if watts:
+        out["socket_power_w_mean"] = round(statistics.fmean(watts), 1)
+        out["socket_power_w_max"] = round(max(watts), 1)
+        out["power_cap_w"] = reader.power_cap_w()
+    if ppt0 and ppt1 and ppt1[0] > ppt0[0]:
+        out["power_limit_active_frac"] = round((ppt1[1] - ppt0[1]) / (ppt1[0] - ppt0[0]), 3)
+    return out
 
 
 def kernel_source_sha256(source):

@@ -291,7 +291,8 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
                   for (int i = 0; i < 8; ++i) {
                     float x = fmaf(S[8 * e8 + i], c, -lv[i]);
                     if (ALIBI) x = fmaf(-sl2, (float)abs(qv[i] - my_kpos), x);
-                    const bool vis = (q0 + r0 + i < Lq) && key_ok && (!causal || my_kpos <= qv[i]);
+                    // bitwise, not short-circuit: no branch per element
+                    const bool vis = (q0 + r0 + i < Lq) & key_ok & (!causal | (my_kpos <= qv[i]));
                     p[8 * e8 + i] = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
                   }
                 } else if constexpr (ALIBI) {
@@ -517,7 +518,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
             for (int i = 0; i < 8; ++i) {
               float x = fmaf(S[8 * e8 + i], c, -my_lse2);
               if (ALIBI) x = fmaf(-sl2, (float)abs(my_pos - kv8[i]), x);
-              const bool vis = (kv0 + j0 + i < Lkv) && (!causal || kv8[i] <= my_pos);
+              // bitwise, not short-circuit: no branch per element
+              const bool vis = (kv0 + j0 + i < Lkv) & (!causal | (kv8[i] <= my_pos));
               const float p = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
               ds[i] = p * (dP[8 * e8 + i] - my_del);
             }
