@@ -119,19 +119,22 @@ class ClockReader:
         return (acc, ppt) if isinstance(acc, int) and isinstance(ppt, int) else None
 
 
-def clock_window(step, reader, seconds, ms_per_step):
+def clock_window(step, reader, seconds, ms_per_step, settle=1.0):
     """The shader clock and socket power under the same load: after the timed
     region, run untimed steps for about `seconds`, keeping two steps in
-    flight, and read the clock and power after each (the metrics table
-    refreshes a few times per second: the clock is averaged over its distinct
-    readings, the power over all of them); plus the fraction of the window in
-    which the package power limit was holding the clock down."""
+    flight, and read the clock and power after each. The device's metrics
+    table refreshes only now and then, so readings from the first `settle`
+    seconds (which may still describe the idle gap before the window) are
+    dropped; the clock is averaged over the distinct readings left, the power
+    over all of them. The package power limit's active fraction comes from the
+    violation counters read at `settle` and at the end."""
     if reader.read() is None:
         return None
     n = max(20, int(seconds * 1e3 / max(ms_per_step, 1e-3)))
     done = []
     samples = []
-    ppt0 = ppt1 = None
+    ppt0 = None
+    t0 = time.perf_counter()
     for i in range(n):
         step(False)
         ev = torch.cuda.Event()
@@ -139,23 +142,23 @@ def clock_window(step, reader, seconds, ms_per_step):
         done.append(ev)
         if i >= 2:
             done[i - 2].synchronize()
-            v = reader.read()
-            if v is not None:
-                samples.append(v)
-        if i == n // 5:
-            ppt0 = reader.ppt_counters()
+            if time.perf_counter() - t0 >= settle:
+                if ppt0 is None:
+                    ppt0 = reader.ppt_counters()
+                v = reader.read()
+                if v is not None:
+                    samples.append(v)
     ppt1 = reader.ppt_counters()
     torch.cuda.synchronize()
     if not samples:
         return None
-    body = samples[len(samples) // 5:]  # the first reads may predate the load
-    distinct = [v for k, v in enumerate(body) if k == 0 or v != body[k - 1]]
+    distinct = [v for k, v in enumerate(samples) if k == 0 or v != samples[k - 1]]
     mhz = [v[0] for v in distinct]
-    watts = [v[1] for v in body if v[1] is not None]
+    watts = [v[1] for v in samples if v[1] is not None]
     out = {"gfx_mhz_mean": round(statistics.fmean(mhz), 1), "gfx_mhz_min": round(min(mhz), 1),
            "gfx_mhz_max": round(max(mhz), 1), "readings": len(distinct), "window_steps": n,
            "source": "amdsmi gpu metrics (current_gfxclks, current_socket_power) and violation status, "
-                     "untimed steps after the timed region"}
+                     f"untimed steps after the timed region, readings after the first {settle:g} s"}
     if watts:
         out["socket_power_w_mean"] = round(statistics.fmean(watts), 1)
         out["socket_power_w_max"] = round(max(watts), 1)
@@ -351,7 +354,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    clk = None if args.no_clock else clock_window(step, ClockReader(), 1.5, ms_per_step)
+    clk = None if args.no_clock else clock_window(step, ClockReader(), 3.0, ms_per_step)
 
     pairs = visible_pairs_per_chunk(w, pos.cpu())
     fwd_flops = 4.0 * d * hq * b * sum(pairs)
