@@ -466,8 +466,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-#pragma clang loop unroll(disable)
-  for (int kv0 = 0, t = 0;; kv0 += TROWS, ++t) {
+  // One key tile; false when the walk ends. FULL: a tile that every row of
+  // the work-group sees in full, whose body then has no mask test at all (a
+  // per-tile test inside the block loop splits it into branches the
+  // scheduler cannot interleave across).
+  auto tile_step = [&](int kv0, int t, auto full_tag) -> bool {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int buf = t & 1;
     // The next tile is copied whenever it exists; whether any query of the
     // work-group sees it is decided once its positions are in LDS.
@@ -486,7 +490,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
       // for ALiBi without the causal mask. Under the causal mask the ALiBi
       // term of a tile the wave sees in full is -slope * (q_pos - k_pos): its
       // key part is S's start value and its row part joins the LSE offset.
-      const bool diag = (kv0 + TROWS > Lkv) || (causal && klast > qmin_w) || (ALIBI && !(causal && lin_ok));
+      const bool diag =
+          !FULL && ((kv0 + TROWS > Lkv) || (causal && klast > qmin_w) || (ALIBI && !(causal && lin_ok)));
       const float row_off = ALIBI ? -my_lse2 - sl2 * (float)(my_pos - kfirst) : -my_lse2;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
@@ -542,12 +547,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
         }
       }
     }
-    if (!have_next) break;
+    if (!have_next) return false;
     store_kp(buf ^ 1, kv0 + TROWS, kp_next);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (causal && uniform_i(kp[buf ^ 1][0]) > qmax_wg) break;  // keys past the last query
+    // keys past the last query end the walk
+    return !(causal && uniform_i(kp[buf ^ 1][0]) > qmax_wg);
+  };
+  // The leading tiles every row of the work-group sees in full (complete
+  // tiles whose last key is at most its first query), then the rest.
+  int T1 = 0;
+  if (!ALIBI || (causal && lin_ok)) {
+    const int nfull = Lkv / TROWS;
+    const int qmin_wg = a.q_pos[q0];
+    T1 = causal ? prefix_count(nfull, lane, [&](int u) { return kpos[u * TROWS + TROWS - 1] <= qmin_wg; }) : nfull;
   }
+  bool more = true;
+  int kv0 = 0, t = 0;
+#pragma clang loop unroll(disable)
+  for (; more && t < T1; kv0 += TROWS, ++t) more = tile_step(kv0, t, std::true_type{});
+#pragma clang loop unroll(disable)
+  for (; more; kv0 += TROWS, ++t) more = tile_step(kv0, t, std::false_type{});
 
   if (!touched || !row_ok) return;
   // dq_acc += scale * dQ; element (dt, e) of this lane is dim 32*dt +
