@@ -9,8 +9,8 @@
 // exp(m_old - m_new) and every term taken against the same reference max.
 //
 // How it maps onto the MI355X:
-//  * One 512-thread work-group (8 waves) owns 256 query rows of one head;
-//    each wave owns 32 rows. K/V stream through LDS in tiles of 64 keys,
+//  * One 512-thread work-group (8 waves) works on 256 query rows of one head
+//    at a time; each wave owns 32 rows. K/V stream through LDS in tiles of 64 keys,
 //    moved global -> LDS by the DMA path (global_load_lds_dwordx4, no
 //    register staging). Rows past the end of the chunk are clamped to the
 //    last key and masked.
@@ -72,8 +72,11 @@
 //    in the key position, so it becomes one per-key term staged in LDS (the
 //    start value of the QK accumulators in the ping-pong loop) plus one
 //    per-row constant.
-//  * Work-groups are ordered heaviest-first and, when the counts allow, each
-//    XCD is given whole heads so that its L2 serves one head's K/V stream.
+//  * The launch is persistent: at most one work-group per CU, each walking a
+//    fixed list of query tiles, so that no CU waits for a second dispatch.
+//    Each XCD's work-groups share a range of whole heads (its L2 serves their
+//    K/V stream), and the tiles are dealt heaviest first in snake order so
+//    that every work-group gets a similar sum of work.
 //  * K and V tiles are stored as 64-column halves with XOR-swizzled 16-byte
 //    chunks, so that neither the K row reads nor the transposing V reads meet
 //    a bank conflict and the fragment addresses keep folding into immediate
@@ -157,8 +160,7 @@ __device__ __forceinline__ void tile_counts(const int* kpos, int na, int ba, int
 }
 
 template <int D, bool ALIBI>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n_qtiles,
-                                                                int xcd_remap) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n_qtiles, int groups) {
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
   constexpr int KK = D / 16;            // k-steps of the QK product
   constexpr int DT = D / 32;            // 32-row d tiles of O^T
@@ -174,21 +176,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   __shared__ __align__(16) float kbc[ALIBI ? 4 : 1][BN];
   __shared__ int kbase[4];  // position of the first key of the tile in kb[]
 
-  const int Lq = a.len_q, Lkv = a.len_kv;
   const int BH = a.batch * a.heads_q;
-  int task = blockIdx.x;
-  if (xcd_remap) {
-    const int per = (n_qtiles * BH) >> 3;
-    task = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  }
-  const int bh = task / n_qtiles;
-  const int qt = n_qtiles - 1 - (task - bh * n_qtiles);
-  const int b = bh / a.heads_q, h = bh - b * a.heads_q;
-  const int hk = h / (a.heads_q / a.heads_kv);
 
-  const int tid = threadIdx.x;
+  // One query tile (256 rows of one head) of the step; the work-group walks
+  // a list of them (see the loop at the end).
+  using CArgs = const __attribute__((address_space(4))) StepArgs;
+  auto run_task = [&](CArgs& a, const int tid, const int bh_in, const int qt_in) {
+  // Uniform across the work-group; said so, so that addresses derived from them stay scalar.
+  const int bh = uniform_i(bh_in), qt = uniform_i(qt_in);
   const int wave = uniform_i(tid >> 6), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int set = wave >> 2;  // two sets of 4 waves, half a tile apart
+  const int Lq = a.len_q, Lkv = a.len_kv;
+  const int b = bh / a.heads_q, h = bh - b * a.heads_q;
+  const int hk = h / (a.heads_q / a.heads_kv);
   const int q0 = qt * BM, q0w = q0 + wave * 32;
   const int row = q0w + l32;
   const bool row_ok = row < Lq;
@@ -689,16 +689,68 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
     mh[row] = m_ref * RA_LN2;
     lh[row] = l_tot;
   }
+  };
+
+  // Persistent walk: the grid holds at most one work-group per CU, split into
+  // `groups` groups (work-group i runs on XCD i % 8, so with 8 groups each
+  // group is one XCD) that each own a contiguous range of heads, so that an
+  // XCD's L2 serves the K/V stream of few heads. A group's query tiles are
+  // ordered heaviest first (under the causal mask a tile's work grows with
+  // its position) and dealt out to its work-groups in snake order -- forward
+  // in even rounds, backward in odd ones -- so that every work-group gets a
+  // similar mix of heavy and light tiles and no second dispatch is needed.
+  const int x = (int)blockIdx.x % groups, slot = (int)blockIdx.x / groups;
+  const int S = (int)gridDim.x / groups;
+  const int hpg = BH / groups;
+  const int M = hpg * n_qtiles;
+  // The arguments and the thread index pass through registers that the
+  // optimizer cannot see through, once per tile: values derived from them are
+  // then computed inside the tile instead of being held in registers across
+  // the whole walk.
+  auto args = [&]() {
+    CArgs* ap = (CArgs*)__builtin_amdgcn_kernarg_segment_ptr();  // `a` is the first argument
+    asm volatile("" : "+s"(ap));
+    return ap;
+  };
+  auto thread = [&]() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t & (kThreads - 1);
+  };
+  for (int k = 0; (k >> 1) * 2 * S < M; ++k) {
+    const int i = (k >> 1) * 2 * S + ((k & 1) ? 2 * S - 1 - slot : slot);
+    if (i >= M) continue;
+    run_task(*args(), thread(), x * hpg + i % hpg, n_qtiles - 1 - i / hpg);
+    __syncthreads();  // the next tile reuses the LDS buffers
+  }
+}
+
+// Work-groups of the persistent forward launch: one per CU at most.
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 template <int D, bool ALIBI>
 hipError_t launch_d(const StepArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.len_q + BM - 1) / BM;
-  const int64_t grid = (int64_t)n_qtiles * a.batch * a.heads_q;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
-  const int remap = (grid % 8 == 0) ? 1 : 0;
+  const int64_t tasks = (int64_t)n_qtiles * a.batch * a.heads_q;
+  if (tasks > INT32_MAX) return hipErrorInvalidValue;
+  const int bh = a.batch * a.heads_q;
+  const int ncu = cu_count();
+  int grid, groups;
+  if (tasks <= ncu) {
+    grid = (int)tasks;  // one tile each
+    groups = (bh % 8 == 0) ? 8 : 1;
+  } else {
+    groups = (bh % 8 == 0 && ncu % 8 == 0) ? 8 : 1;
+    grid = ncu;
+  }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, ALIBI>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     a, n_qtiles, remap);
+                     a, n_qtiles, groups);
   return hipGetLastError();
 }
 
