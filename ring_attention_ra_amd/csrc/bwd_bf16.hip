@@ -366,21 +366,25 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
   }
 
   // Accumulate into dv_blk (dV wave) or dk_blk (dK wave): element (dt, e) is
-  // key kw0 + 8*(e/4) + 4*hf + e%4, dim 32*dt + l32.
+  // key kw0 + 8*(e/4) + 4*hf + e%4, dim 32*dt + l32. Through a buffer
+  // resource that starts at the wave's first key and ends at the chunk's
+  // end, so that rows past it read zeros and drop their stores with no
+  // branch; all 64 loads are issued before the first sum, so the wave waits
+  // for memory once rather than once per element.
   if (!wave_active) return;
-  float* outh = (dv_wave ? a.dv : a.dk) + khead * Lkv * D;
+  const auto rout = make_rsrc((dv_wave ? a.dv : a.dk) + (khead * Lkv + kw0) * D, (int64_t)(Lkv - kw0) * D * 4);
   const float f = dv_wave ? 1.0f : a.scale;
+  auto out_off = [&](int dt, int e) { return (uint32_t)(((8 * (e >> 2) + 4 * hf + (e & 3)) * D + 32 * dt + l32) * 4); };
+  float old[DT][16];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kr = kw0 + 8 * (e >> 2) + 4 * hf + (e & 3);
-      if (kr < Lkv) {
-        const int64_t idx = (int64_t)kr * D + 32 * dt + l32;
-        outh[idx] += f * acc[dt][e];
-      }
-    }
-  }
+    for (int e = 0; e < 16; ++e) old[dt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rout, out_off(dt, e), 0, 0));
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(f, acc[dt][e], old[dt][e])), rout, out_off(dt, e), 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -569,23 +573,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
 #pragma clang loop unroll(disable)
   for (; more; kv0 += TROWS, ++t) more = tile_step(kv0, t, std::false_type{});
 
-  if (!touched || !row_ok) return;
+  if (!touched) return;
   // dq_acc += scale * dQ; element (dt, e) of this lane is dim 32*dt +
-  // 8*(e/4) + 4*hf + e%4 of query `row`.
-  float* dqr = a.dq + (qhead * Lq + row) * D;
+  // 8*(e/4) + 4*hf + e%4 of query `row`. Through a buffer resource from the
+  // work-group's first row to the chunk's end (rows past it read zeros and
+  // drop their stores), all loads before the first sum.
+  const auto rdq = make_rsrc(a.dq + (qhead * Lq + q0) * D, (int64_t)(Lq - q0) * D * 4);
+  auto dq_off = [&](int dt, int a4) { return (uint32_t)(((row - q0) * D + 32 * dt + 8 * a4 + 4 * hf) * 4); };
+  uint4 old[DT][4];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      float4* p = reinterpret_cast<float4*>(dqr + 32 * dt + 8 * a4 + 4 * hf);
-      float4 v = *p;
-      v.x += a.scale * dQ[dt][4 * a4 + 0];
-      v.y += a.scale * dQ[dt][4 * a4 + 1];
-      v.z += a.scale * dQ[dt][4 * a4 + 2];
-      v.w += a.scale * dQ[dt][4 * a4 + 3];
-      *p = v;
-    }
-  }
+    for (int a4 = 0; a4 < 4; ++a4) old[dt][a4] = buf_load16(rdq, dq_off(dt, a4));
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4)
+      buf_store16(rdq, dq_off(dt, a4), fmaf(a.scale, dQ[dt][4 * a4 + 0], __uint_as_float(old[dt][a4].x)),
+                  fmaf(a.scale, dQ[dt][4 * a4 + 1], __uint_as_float(old[dt][a4].y)),
+                  fmaf(a.scale, dQ[dt][4 * a4 + 2], __uint_as_float(old[dt][a4].z)),
+                  fmaf(a.scale, dQ[dt][4 * a4 + 3], __uint_as_float(old[dt][a4].w)));
 }
 
 template <bool ALIBI>
