@@ -282,64 +282,87 @@ def main():
         dv = torch.empty_like(dk)
     sched = ring.ring_schedule(n, w.rank)
     stream = torch.cuda.current_stream()
-
     side = torch.cuda.Stream(device=dev)  # default priority
+
+    # Every library call of a step is checked and marshalled once here
+    # (_lib.bind); the loop then only re-issues the calls, so that on the
+    # short chunks the host keeps ahead of the GPU.
+    bind = _lib.bind
+    perm_own = [bind(_lib.ra_layout_permute, q_g, q_loc, None, b * hq, s, d, n, w.layout, rank=w.rank)]
+    if args.serial_permute:
+        perm_own += [bind(_lib.ra_layout_permute, k_g, k_ch, pos, b * hkv, s, d, n, w.layout, rank=-1),
+                     bind(_lib.ra_layout_permute, v_g, v_ch, None, b * hkv, s, d, n, w.layout, rank=-1)]
+    else:
+        perm_own += [bind(_lib.ra_layout_permute, k_g, k_ch[w.rank], pos[w.rank], b * hkv, s, d, n, w.layout,
+                          rank=w.rank),
+                     bind(_lib.ra_layout_permute, v_g, v_ch[w.rank], None, b * hkv, s, d, n, w.layout,
+                          rank=w.rank)]
+    # The next chunk in ring order is permuted on the side stream while a
+    # step runs, the way it would arrive during it.
+    perm_side = {nxt: [bind(_lib.ra_layout_permute, k_g, k_ch[nxt], pos[nxt], b * hkv, s, d, n, w.layout,
+                            rank=nxt, stream=side),
+                       bind(_lib.ra_layout_permute, v_g, v_ch[nxt], None, b * hkv, s, d, n, w.layout, rank=nxt,
+                            stream=side)]
+                 for nxt in sched[1:]}
+    init_call = bind(_lib.ra_state_init, dims, o_acc, m, l)
+    fwd_calls = [bind(_lib.ra_step_fwd, dims, q_loc, k_ch[src], v_ch[src], pos[w.rank], pos[src], w.causal,
+                      w.scale, slopes, o_acc, m, l) for src in sched]
+    fin_call = bind(_lib.ra_finalize, dims, o_acc, m, l, o, lse)
+    if w.backward:
+        delta_call = bind(_lib.ra_bwd_delta, dims, o, d_o, delta)
+        bwd_calls = [bind(_lib.ra_step_bwd, dims, q_loc, k_ch[src], v_ch[src], pos[w.rank], pos[src], w.causal,
+                          w.scale, slopes, d_o, lse, delta, dq, dk[src], dv[src]) for src in sched]
+    # Events that only order the two streams, reused every step.
+    go = [torch.cuda.Event() for _ in sched]
+    ready = [torch.cuda.Event() for _ in sched]
+
     fwd_events, bwd_events, perm_events, side_events, step_events = [], [], [], [], []
+    pool = []  # timing events, created before the timed steps
 
     def ev(on=None):
-        e = torch.cuda.Event(enable_timing=True)
+        e = pool.pop() if pool else torch.cuda.Event(enable_timing=True)
         e.record(stream if on is None else on)
         return e
 
     def step(timed):
-        ready = {}
         if timed:
             step_events.append(ev())
             perm_events.append(ev())
-        _lib.ra_layout_permute(q_g, q_loc, None, b * hq, s, d, n, w.layout, rank=w.rank)
-        if args.serial_permute:
-            _lib.ra_layout_permute(k_g, k_ch, pos, b * hkv, s, d, n, w.layout, rank=-1)
-            _lib.ra_layout_permute(v_g, v_ch, None, b * hkv, s, d, n, w.layout, rank=-1)
-        else:
-            _lib.ra_layout_permute(k_g, k_ch[w.rank], pos[w.rank], b * hkv, s, d, n, w.layout, rank=w.rank)
-            _lib.ra_layout_permute(v_g, v_ch[w.rank], None, b * hkv, s, d, n, w.layout, rank=w.rank)
+        for call in perm_own:
+            call()
         if timed:
             perm_events.append(ev())
-        _lib.ra_state_init(dims, o_acc, m, l)
-        for j, src in enumerate(sched):
+        init_call()
+        for j in range(n):
             if j > 0 and not args.serial_permute:
-                stream.wait_event(ready[src])
+                stream.wait_event(ready[j])
             if not args.serial_permute and j + 1 < n:
-                # The next chunk in ring order is permuted on the side stream
-                # while this step runs, the way it would arrive during it. It
-                # starts once every earlier use of its buffers (all on the
+                # It starts once every earlier use of its buffers (all on the
                 # launch stream) is behind it.
-                nxt = sched[j + 1]
-                side.wait_event(ev())
+                go[j + 1].record(stream)
+                side.wait_event(go[j + 1])
                 if timed:
                     side_events.append(ev(side))
-                _lib.ra_layout_permute(k_g, k_ch[nxt], pos[nxt], b * hkv, s, d, n, w.layout, rank=nxt, stream=side)
-                _lib.ra_layout_permute(v_g, v_ch[nxt], None, b * hkv, s, d, n, w.layout, rank=nxt, stream=side)
-                ready[nxt] = ev(side)
+                for call in perm_side[sched[j + 1]]:
+                    call()
+                ready[j + 1].record(side)
                 if timed:
-                    side_events.append(ready[nxt])
+                    side_events.append(ev(side))
             if timed:
                 fwd_events.append(ev())
-            _lib.ra_step_fwd(dims, q_loc, k_ch[src], v_ch[src], pos[w.rank], pos[src], w.causal, w.scale,
-                             slopes, o_acc, m, l)
+            fwd_calls[j]()
             if timed:
                 fwd_events.append(ev())
-        _lib.ra_finalize(dims, o_acc, m, l, o, lse)
+        fin_call()
         if w.backward:
-            _lib.ra_bwd_delta(dims, o, d_o, delta)
+            delta_call()
             dq.zero_()
             dk.zero_()
             dv.zero_()
-            for src in sched:
+            for j in range(n):
                 if timed:
                     bwd_events.append(ev())
-                _lib.ra_step_bwd(dims, q_loc, k_ch[src], v_ch[src], pos[w.rank], pos[src], w.causal, w.scale,
-                                 slopes, d_o, lse, delta, dq, dk[src], dv[src])
+                bwd_calls[j]()
                 if timed:
                     bwd_events.append(ev())
         if timed:
@@ -347,6 +370,8 @@ def main():
 
     for _ in range(args.warmup):
         step(False)
+    per_step = 4 + 2 * n + (2 * (n - 1) if not args.serial_permute else 0) + (2 * n if w.backward else 0)
+    pool.extend(torch.cuda.Event(enable_timing=True) for _ in range(per_step * args.steps))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):

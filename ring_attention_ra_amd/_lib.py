@@ -4,10 +4,13 @@ Argument marshalling only: tensors are checked for device, dtype, shape and
 contiguity, then their device pointers and the current HIP stream are passed
 to the C ABI. Every computation happens in the library's HIP kernels. If the
 library has not been built this module raises; there is no fallback.
+bind() does the checking and marshalling of one call once and returns a
+function that repeats the call, for loops that issue the same calls again.
 """
 
 from __future__ import annotations
 
+import contextvars
 import ctypes
 import os
 import re
@@ -91,6 +94,47 @@ def _check(status: int, name: str) -> None:
         raise RaError(status, f"{name}: {lib().ra_last_error().decode()}")
 
 
+# While bind() records a call, the entry points hand their marshalled
+# arguments to it instead of calling the library.
+_RECORDING: contextvars.ContextVar = contextvars.ContextVar("ra_recording", default=None)
+
+
+def _invoke(name: str, *cargs) -> None:
+    rec = _RECORDING.get()
+    if rec is not None:
+        rec.append((name, cargs))
+        return
+    _check(getattr(lib(), name)(*cargs), name)
+
+
+def bind(entry, *args, **kwargs):
+    """Check and marshal the arguments of one call of `entry` (one of the
+    entry-point functions below that return nothing) once, without calling
+    the library; returns a function of no arguments that makes exactly that
+    call (same pointers, sizes and stream) and raises RaError on a non-OK
+    status. The caller keeps the tensors alive and in place. For loops that
+    issue the same calls many times (a ring of steps), where checking the
+    tensors on every call would cost more host time than the GPU spends."""
+    rec: list = []
+    token = _RECORDING.set(rec)
+    try:
+        entry(*args, **kwargs)
+    finally:
+        _RECORDING.reset(token)
+    if len(rec) != 1:
+        raise ValueError(f"{getattr(entry, '__name__', entry)} cannot be bound")
+    name, cargs = rec[0]
+    fn = getattr(lib(), name)
+
+    def call() -> None:
+        status = fn(*cargs)
+        if status != RA_OK:
+            _check(status, name)
+
+    call.__name__ = f"bound_{name}"
+    return call
+
+
 def _ptr(t, name, dtype=None, numel=None, allow_none=False):
     if t is None:
         if allow_none:
@@ -142,8 +186,8 @@ def dims_of(q: torch.Tensor, k_blk: torch.Tensor) -> RaDims:
 
 def ra_positions(seq_len, n_ranks, rank, layout, pos_out, stream=None):
     lay = LAYOUTS.get(layout, layout)
-    _check(lib().ra_positions(seq_len, n_ranks, rank, lay, _ptr(pos_out, "pos_out", torch.int32),
-                              _stream(stream)), "ra_positions")
+    _invoke("ra_positions", seq_len, n_ranks, rank, lay, _ptr(pos_out, "pos_out", torch.int32),
+                              _stream(stream))
 
 
 def ra_layout_permute(src, dst, pos, outer, seq_len, row_elems, n_ranks, layout, rank=-1, inverse=0,
@@ -151,10 +195,10 @@ def ra_layout_permute(src, dst, pos, outer, seq_len, row_elems, n_ranks, layout,
     if src.dtype != dst.dtype:
         raise ValueError("src and dst must have the same dtype")
     lay = LAYOUTS.get(layout, layout)
-    _check(lib().ra_layout_permute(_ptr(src, "src"), _ptr(dst, "dst"),
+    _invoke("ra_layout_permute", _ptr(src, "src"), _ptr(dst, "dst"),
                                    _ptr(pos, "pos", torch.int32, allow_none=True), outer, seq_len,
                                    row_elems, dtype_code(src.dtype), n_ranks, lay, rank, int(inverse),
-                                   _stream(stream)), "ra_layout_permute")
+                                   _stream(stream))
 
 
 def ra_rope(x, y, pos, base=10000.0, stream=None):
@@ -165,46 +209,46 @@ def ra_rope(x, y, pos, base=10000.0, stream=None):
         raise ValueError("x must be [..., L, D]")
     length, d = x.shape[-2], x.shape[-1]
     outer = x.numel() // max(length * d, 1)
-    _check(lib().ra_rope(_ptr(x, "x"), _ptr(y, "y"), _ptr(pos, "pos", torch.int32, length), outer, length, d,
-                         dtype_code(x.dtype), float(base), _stream(stream)), "ra_rope")
+    _invoke("ra_rope", _ptr(x, "x"), _ptr(y, "y"), _ptr(pos, "pos", torch.int32, length), outer, length, d,
+                         dtype_code(x.dtype), float(base), _stream(stream))
 
 
 def ra_state_init(dims, o_acc, m, l, stream=None):
     rows = dims.batch * dims.heads_q * dims.len_q
-    _check(lib().ra_state_init(ctypes.byref(dims), _ptr(o_acc, "o_acc", torch.float32, rows * dims.head_dim),
+    _invoke("ra_state_init", ctypes.byref(dims), _ptr(o_acc, "o_acc", torch.float32, rows * dims.head_dim),
                                _ptr(m, "m", torch.float32, rows), _ptr(l, "l", torch.float32, rows),
-                               _stream(stream)), "ra_state_init")
+                               _stream(stream))
 
 
 def ra_step_fwd(dims, q, k_blk, v_blk, q_pos, k_pos, causal, scale, alibi_slopes, o_acc, m, l, stream=None):
     dt = q.dtype
     rows = dims.batch * dims.heads_q * dims.len_q
     kv = dims.batch * dims.heads_kv * dims.len_kv * dims.head_dim
-    _check(lib().ra_step_fwd(
+    _invoke("ra_step_fwd",
         ctypes.byref(dims), _ptr(q, "q", dt, rows * dims.head_dim), _ptr(k_blk, "k_blk", dt, kv),
         _ptr(v_blk, "v_blk", dt, kv), _ptr(q_pos, "q_pos", torch.int32, dims.len_q),
         _ptr(k_pos, "k_pos", torch.int32, dims.len_kv), int(bool(causal)), float(scale),
         _ptr(alibi_slopes, "alibi_slopes", torch.float32, dims.heads_q, allow_none=True),
         _ptr(o_acc, "o_acc", torch.float32, rows * dims.head_dim), _ptr(m, "m", torch.float32, rows),
-        _ptr(l, "l", torch.float32, rows), _stream(stream)), "ra_step_fwd")
+        _ptr(l, "l", torch.float32, rows), _stream(stream))
 
 
 def ra_finalize(dims, o_acc, m, l, o, lse, stream=None):
     rows = dims.batch * dims.heads_q * dims.len_q
     odt = torch.bfloat16 if dims.dtype == RA_BF16 else torch.float32
-    _check(lib().ra_finalize(
+    _invoke("ra_finalize",
         ctypes.byref(dims), _ptr(o_acc, "o_acc", torch.float32, rows * dims.head_dim),
         _ptr(m, "m", torch.float32, rows), _ptr(l, "l", torch.float32, rows),
         _ptr(o, "o", odt, rows * dims.head_dim, allow_none=True),
-        _ptr(lse, "lse", torch.float32, rows, allow_none=True), _stream(stream)), "ra_finalize")
+        _ptr(lse, "lse", torch.float32, rows, allow_none=True), _stream(stream))
 
 
 def ra_bwd_delta(dims, o, d_o, delta, stream=None):
     rows = dims.batch * dims.heads_q * dims.len_q
     odt = torch.bfloat16 if dims.dtype == RA_BF16 else torch.float32
-    _check(lib().ra_bwd_delta(ctypes.byref(dims), _ptr(o, "o", odt, rows * dims.head_dim),
+    _invoke("ra_bwd_delta", ctypes.byref(dims), _ptr(o, "o", odt, rows * dims.head_dim),
                               _ptr(d_o, "d_o", odt, rows * dims.head_dim),
-                              _ptr(delta, "delta", torch.float32, rows), _stream(stream)), "ra_bwd_delta")
+                              _ptr(delta, "delta", torch.float32, rows), _stream(stream))
 
 
 def ra_step_bwd(dims, q, k_blk, v_blk, q_pos, k_pos, causal, scale, alibi_slopes, d_o, lse, delta,
@@ -212,7 +256,7 @@ def ra_step_bwd(dims, q, k_blk, v_blk, q_pos, k_pos, causal, scale, alibi_slopes
     dt = q.dtype
     rows = dims.batch * dims.heads_q * dims.len_q
     kv = dims.batch * dims.heads_kv * dims.len_kv * dims.head_dim
-    _check(lib().ra_step_bwd(
+    _invoke("ra_step_bwd",
         ctypes.byref(dims), _ptr(q, "q", dt, rows * dims.head_dim), _ptr(k_blk, "k_blk", dt, kv),
         _ptr(v_blk, "v_blk", dt, kv), _ptr(q_pos, "q_pos", torch.int32, dims.len_q),
         _ptr(k_pos, "k_pos", torch.int32, dims.len_kv), int(bool(causal)), float(scale),
@@ -220,7 +264,7 @@ def ra_step_bwd(dims, q, k_blk, v_blk, q_pos, k_pos, causal, scale, alibi_slopes
         _ptr(d_o, "d_o", dt, rows * dims.head_dim), _ptr(lse, "lse", torch.float32, rows),
         _ptr(delta, "delta", torch.float32, rows), _ptr(dq_acc, "dq_acc", torch.float32, rows * dims.head_dim),
         _ptr(dk_blk, "dk_blk", torch.float32, kv), _ptr(dv_blk, "dv_blk", torch.float32, kv),
-        _stream(stream)), "ra_step_bwd")
+        _stream(stream))
 
 
 def ra_count_nonfinite(x, stream=None) -> int:

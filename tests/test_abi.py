@@ -204,3 +204,28 @@ def test_count_nonfinite_validation():
     assert L.ra_count_nonfinite(1, 4, 9, ctypes.byref(n), None) == 1 and "dtype" in _lib.ra_last_error()
     assert L.ra_count_nonfinite(None, 4, 0, ctypes.byref(n), None) == 1 and "NULL" in _lib.ra_last_error()
     assert L.ra_count_nonfinite(None, 0, 0, ctypes.byref(n), None) == 0 and n.value == 0
+
+
+def test_bind_records_one_call_and_defers_it():
+    # A bound call marshals now and calls the library only when invoked; the
+    # invalid call below (NULL output) is rejected by the library's host-side
+    # checks, before any launch.
+    call = _lib.bind(lambda: _lib._invoke("ra_positions", 16, 4, 0, 0, None, None))
+    assert callable(call)
+    with pytest.raises(_lib.RaError) as err:
+        call()
+    assert err.value.status == _lib.RA_ERR_INVALID_ARGUMENT
+    with pytest.raises(ValueError):
+        _lib.bind(lambda: None)  # records no call
+
+    def two_calls():
+        _lib._invoke("ra_positions", 16, 4, 0, 0, None, None)
+        _lib._invoke("ra_positions", 16, 4, 0, 0, None, None)
+
+    with pytest.raises(ValueError):
+        _lib.bind(two_calls)
+    with pytest.raises(ValueError):
+        _lib.bind(_lib.ra_positions, 16, 4, 0, "zigzag", torch.zeros(4, dtype=torch.int32))  # host tensor
+    # recording ended: a direct call reaches the library again
+    with pytest.raises(_lib.RaError):
+        _lib._invoke("ra_positions", 16, 4, 0, 0, None, None)
