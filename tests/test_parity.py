@@ -143,14 +143,28 @@ def test_fwd_bf16_variants(d, layout, causal, alibi, hq, hkv, n, c):
     _check_full(Case("bf16", 1, hq, hkv, d, n * c, n, layout, causal, alibi, seed=21))
 
 
-@pytest.mark.parametrize("layout,causal,alibi,hq,hkv,n,c", [
-    ("zigzag", True, False, 2, 2, 4, 40),          # chunk shorter than one 64-key tile
-    ("contiguous", True, False, 1, 1, 2, 4497),    # 71 key tiles: two rounds of the tile search, ragged
-    ("zigzag", True, False, 2, 2, 2, 4497),
-    ("zigzag", True, True, 2, 1, 2, 4497),         # ALiBi + GQA over the same range
+@pytest.mark.parametrize("layout,causal,alibi,hq,hkv,n,c,ranks", [
+    ("zigzag", True, False, 2, 2, 4, 40, None),          # chunk shorter than one 64-key tile
+    ("contiguous", True, False, 1, 1, 2, 4497, None),    # 71 key tiles, ragged
+    ("zigzag", True, False, 2, 2, 2, 4497, None),
+    ("zigzag", True, True, 2, 1, 2, 4497, None),         # ALiBi + GQA over the same range
+    # chunks longer than any workload's (258 key tiles), ragged
+    ("contiguous", True, False, 1, 1, 2, 16500, [1]),
+    ("zigzag", True, False, 1, 1, 2, 16500, [1]),
 ])
-def test_fwd_bf16_tile_range_edges(layout, causal, alibi, hq, hkv, n, c):
-    _check_full(Case("bf16", 1, hq, hkv, 128, n * c, n, layout, causal, alibi, seed=25))
+def test_fwd_bf16_tile_range_edges(layout, causal, alibi, hq, hkv, n, c, ranks):
+    _check_full(Case("bf16", 1, hq, hkv, 128, n * c, n, layout, causal, alibi, seed=25), ranks=ranks)
+
+
+# The persistent bf16 launch: with fewer query tiles than CUs each work-group
+# takes one tile; with more (the second and third cases on a 256-CU GPU) each
+# walks several, heaviest and lightest in turn (ragged ends, GQA, more than 64
+# key tiles).
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("hq,hkv,n,c", [(2, 1, 2, 4497), (132, 66, 2, 300), (16, 8, 2, 4497)])
+def test_fwd_bf16_one_and_several_tiles_per_work_group(d, layout, hq, hkv, n, c):
+    _check_full(Case("bf16", 1, hq, hkv, d, n * c, n, layout, True, False, seed=29), ranks=[n - 1])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
