@@ -23,10 +23,11 @@
 //    each lane holds one key and 8 consecutive queries per k-step), which
 //    makes P^T and dS^T ready-made A operands of the next products; dO and Q
 //    are read with the transposing LDS read.
-//  * bwd_dq_kernel: a work-group owns 128 queries (4 waves x 32) and walks the
-//    key tiles, like the forward step: S^T = K Q^T and dP^T = V dO^T (Q and dO
-//    fragments in registers), then dQ^T += K^T dS^T with K^T from the
-//    transposing read.
+//  * bwd_dq_kernel: a work-group takes 128 queries (4 waves x 32) at a time and
+//    walks the key tiles, like the forward step: S^T = K Q^T and dP^T = V dO^T
+//    (Q and dO fragments in registers), then dQ^T += K^T dS^T with K^T from the
+//    transposing read. The launch is persistent (two work-groups per CU at
+//    most), with each XCD taking its heads one at a time, as in the forward.
 // Tiles stream through double-buffered LDS via the DMA path; fully masked
 // tiles are skipped from the positions (which increase), and only tiles
 // across the diagonal (or ragged, or with ALiBi) are masked per element.
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkdv_kernel(BwdArgs a, int 
 // ---------------------------------------------------------------------------
 
 template <bool ALIBI>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int groups) {
   __shared__ uint4 Ks[2][SLOTS];
   __shared__ uint4 Vs[2][SLOTS];
   __shared__ __align__(16) int kp[2][TROWS];
@@ -400,17 +401,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
   // start value of S on the tiles the wave sees in full.
   __shared__ __align__(16) float kbc[ALIBI ? 2 : 1][TROWS];
 
+  const int BH = a.batch * a.heads_q;
+
+  // One 128-query tile of one head; the work-group walks a list of them (see
+  // the loop at the end).
+  using CArgs = const __attribute__((address_space(4))) BwdArgs;
+  auto run_task = [&](CArgs& a, const int tid, const int bh_in, const int qt_in) {
+  // Uniform across the work-group; said so, so that addresses derived from them stay scalar.
+  const int bh = uniform_i(bh_in), qt = uniform_i(qt_in);
   const int Lq = a.len_q, Lkv = a.len_kv;
-  // Query tiles in order of decreasing work across all heads (the last tile
-  // sees the most keys under the causal mask); head bh lands on XCD bh % 8.
-  const int n_bh = (int)(gridDim.x / (unsigned)n_qtiles);
-  const int w = blockIdx.x / n_bh;
-  const int bh = blockIdx.x - w * n_bh;
-  const int qt = n_qtiles - 1 - w;
   const int b = bh / a.heads_q, h = bh - b * a.heads_q;
   const int hk = h / (a.heads_q / a.heads_kv);
-
-  const int tid = threadIdx.x;
   const int wave = uniform_i(tid >> 6), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int q0 = qt * 128, q0w = q0 + 32 * wave;
   const int row = q0w + l32;
@@ -593,6 +594,41 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int n_qt
                   fmaf(a.scale, dQ[dt][4 * a4 + 1], __uint_as_float(old[dt][a4].y)),
                   fmaf(a.scale, dQ[dt][4 * a4 + 2], __uint_as_float(old[dt][a4].z)),
                   fmaf(a.scale, dQ[dt][4 * a4 + 3], __uint_as_float(old[dt][a4].w)));
+  };
+
+  // Persistent walk, as in the forward step: at most two work-groups per CU,
+  // split into `groups` groups (work-group i runs on XCD i % 8) that each own
+  // a contiguous range of heads, listed head by head with each head's
+  // heaviest tiles first (under the causal mask a query tile's work grows
+  // with its position) and dealt to the group's work-groups in snake order,
+  // so that every work-group gets a similar sum of work and an XCD's
+  // work-groups stream the K/V of one head at a time. The arguments reach
+  // each tile through a pointer the optimizer cannot see through, so that
+  // values derived from them are not held across the walk.
+  const int x = (int)blockIdx.x % groups, slot = (int)blockIdx.x / groups;
+  const int S = (int)gridDim.x / groups;
+  const int hpg = BH / groups;
+  const int M = hpg * n_qtiles;
+  auto args = [&]() {
+    CArgs* ap = (CArgs*)__builtin_amdgcn_kernarg_segment_ptr();  // `a` is the first argument
+    asm volatile("" : "+s"(ap));
+    return ap;
+  };
+  for (int k = 0; (k >> 1) * 2 * S < M; ++k) {
+    const int i = (k >> 1) * 2 * S + ((k & 1) ? 2 * S - 1 - slot : slot);
+    if (i >= M) continue;
+    run_task(*args(), (int)threadIdx.x, x * hpg + i / n_qtiles, n_qtiles - 1 - i % n_qtiles);
+    __syncthreads();  // the next tile reuses the LDS buffers
+  }
+}
+
+// CUs of the current device (256 if the runtime cannot say).
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 template <bool ALIBI>
@@ -602,7 +638,18 @@ hipError_t launch_both(const BwdArgs& a, hipStream_t stream) {
   const int64_t grid_q = (int64_t)n_qtiles * a.batch * a.heads_q;
   const int64_t grid_k = (int64_t)n_ktiles * a.batch * a.heads_kv;
   if (grid_q > INT32_MAX || grid_k > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dq_kernel<ALIBI>), dim3((unsigned)grid_q), dim3(kThreads), 0, stream, a, n_qtiles);
+  // dQ: persistent, two work-groups per CU at most.
+  const int bhq = a.batch * a.heads_q;
+  const int slots = 2 * cu_count();
+  int gq, groups;
+  if (grid_q <= slots) {
+    gq = (int)grid_q;  // one tile each
+    groups = (bhq % 8 == 0) ? 8 : 1;
+  } else {
+    groups = (bhq % 8 == 0 && slots % 8 == 0) ? 8 : 1;
+    gq = slots;
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<ALIBI>), dim3((unsigned)gq), dim3(kThreads), 0, stream, a, n_qtiles, groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<ALIBI>), dim3((unsigned)grid_k), dim3(kThreadsKV), 0, stream, a,
