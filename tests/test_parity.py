@@ -394,6 +394,11 @@ def test_bwd_variants(layout, causal, alibi, hq, hkv, n, c):
     # one 16384-row chunk attending to itself: the dK / dV of key 0 is a sum
     # over all 16384 rows, the length of a full-size chunk.
     ("contiguous", False, 1, 1, 1, 16384, (0,)),
+    # 176 query heads over 22 K/V heads, ragged chunks of 300: 528 query tiles
+    # of 128 rows, more than the persistent dQ launch has work-groups on a
+    # 256-CU GPU, so each walks several (both layouts, with and without ALiBi).
+    ("zigzag", False, 176, 22, 2, 300, (1,)),
+    ("contiguous", True, 176, 22, 2, 300, (1,)),
 ])
 def test_bwd_long_sums_full(layout, alibi, hq, hkv, n, c, ranks):
     case = Case("bf16", 1, hq, hkv, 128, n * c, n, layout, True, alibi, seed=65)
